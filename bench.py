@@ -1,0 +1,259 @@
+"""Dispatch+combine benchmark on one MI355X.
+
+One step = router stand-in output already on the GPU -> dispatch (plan, pack, exchange)
+-> expert stand-in (harness, not in the metric) -> combine (return exchange, combine),
+over one batch of seeded synthetic input resident in HBM.  The default workload is the
+prefill shape: 8 virtual ranks x 8192 tokens, hidden 5120 bf16, 128 experts (16 per
+rank), top-1 with Zipf(1.2) expert popularity.
+
+Printed: ONE JSON line.  `value` is the effective HBM bandwidth of dispatch+combine, the
+algorithmic bytes of the staged path ((2N + 6A) rows of real tokens) divided by the
+dispatch+combine time from HIP events recorded between the library's kernels on the
+stream they run on; `us_per_step` is that time; `ms_per_step` is the wall time of a
+whole step (expert stand-in included) between two synchronisations.  `roofline` is for
+the slowest kernel of the step; `cpu_baseline` is the CPU oracle on a bounded sample of
+the same workload; `decode_graph` is the decode shape captured in a hipGraph and
+replayed with routing that changes on the device each step.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def stage_bytes(w):
+    """Algorithmic bytes per launch of each stage (real rows only)."""
+    N, A, row = w.tokens, w.assignments, w.row_bytes
+    return {
+        "plan": A * 4 + 4 * (w.num_ranks * w.num_experts + 3 * w.num_ranks * (w.num_ranks + 1)) + A * 8,
+        "pack": (N + A) * row + A * 4,
+        "exchange": 2 * A * row,
+        "return": 2 * A * row,
+        "combine": (A + N) * row + A * 8,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode-graph", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the R virtual ranks live in one GPU's HBM and no "
+              f"collective crosses GPUs, so --gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from moe_alltoallv_resident_amd import a2av
+    from moe_alltoallv_resident_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    w = W.workload(args.workload)
+    log(f"workload {w.describe()}; generating inputs")
+    x, ids, gates = W.make_inputs(w)
+    if w.dtype == W.BF16:
+        xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    else:
+        xt = torch.from_numpy(x).cuda()
+    idt = torch.from_numpy(ids).cuda()
+    gt = torch.from_numpy(gates).cuda()
+    s = a2av.Session(w.num_ranks, w.tokens_per_rank, w.hidden, w.dtype, w.experts_per_rank, w.top_k,
+                     w.recv_capacity_rows)
+    y = torch.empty_like(xt)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        s.dispatch(xt, idt)
+        s.expert(s.recv, s.recv, w.expert_mode)
+        s.combine(s.recv, gt, y)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    log(f"timing {args.steps} steps")
+    a2av.a2av_timing_begin(s.handle, args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_sum, launches = a2av.a2av_timing_end(s.handle)
+    status = int(s.status.item())
+    if status != 0:
+        raise RuntimeError(f"device status {status} during the benchmark")
+    stage_ms = {n: ms_sum[i] / max(1, launches[i]) for i, n in enumerate(a2av.STAGE_NAMES)}
+    dc_ms = sum(stage_ms.values())
+    staged = w.staged_bytes()
+    gbps = staged / (dc_ms * 1e-3) / 1e9
+    sb = stage_bytes(w)
+    dom = max((n for n in stage_ms if n != "plan"), key=lambda n: stage_ms[n])
+    dom_gbps = sb[dom] / (stage_ms[dom] * 1e-3) / 1e9
+    log("stages (ms/launch): " + ", ".join(f"{n} {v:.4f}" for n, v in stage_ms.items()))
+
+    # achievable reference: a plain device copy of one stage's bytes (read + write)
+    ref_elems = w.assignments * w.row_bytes // 2
+    src = torch.empty(ref_elems, dtype=torch.int16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * ref_elems * 2 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+
+    result = {
+        "metric": "dispatch+combine µs/step and effective HBM GB/s (% of peak), 1 MI355X",
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "us_per_step": round(dc_ms * 1e3, 2),
+        "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == W.BF16 else "f32",
+        "data": "synthetic (seeded numpy; no model weights or traces)",
+        "config": {
+            "workload": w.describe(),
+            "virtual_ranks": w.num_ranks, "tokens_per_rank": w.tokens_per_rank, "hidden": w.hidden,
+            "experts": w.num_experts, "top_k": w.top_k, "path": "staged (pack, exchange, return, combine)",
+            "algorithmic_bytes_per_step": staged,
+        },
+        "stage_us": {n: round(v * 1e3, 2) for n, v in stage_ms.items()},
+        "roofline": {
+            "bound": "hbm", "kernel": dom, "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+            "bytes_per_launch": sb[dom], "copy_reference_GBps": round(copy_gbps, 1),
+        },
+    }
+    s.close()
+    del xt, y, s
+    torch.cuda.empty_cache()
+
+    if not args.no_decode_graph:
+        result["decode_graph"] = decode_graph(np, torch, a2av, W)
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(np, W, w, args.cpu_sample_tokens)
+
+    print(json.dumps(result), flush=True)
+
+
+def decode_graph(np, torch, a2av, W, steps=100):
+    """Decode shape: one hipGraph of router stand-in -> dispatch -> expert -> combine,
+    replayed `steps` times with fresh routing taken on the device; one event pair around
+    all replays, no host synchronisation between them."""
+    w = W.workload("decode")
+    log(f"decode graph: {w.describe()}, {steps} replays")
+    x = W.make_x(w)
+    n = w.tokens * w.top_k
+    ids_table = torch.from_numpy(np.stack([W.make_ids(w, i).reshape(n) for i in range(steps)])).cuda()
+    gates_table = torch.from_numpy(np.stack([W.make_gates(w, i).reshape(n) for i in range(steps)])).cuda()
+    xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    counter = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ids = torch.empty((w.num_ranks, w.tokens_per_rank, w.top_k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((w.num_ranks, w.tokens_per_rank, w.top_k), dtype=torch.float32, device="cuda")
+    y = torch.empty_like(xt)
+    s = a2av.Session(w.num_ranks, w.tokens_per_rank, w.hidden, w.dtype, w.experts_per_rank, w.top_k)
+
+    def step():
+        a2av.a2av_route_step(ids_table, gates_table, steps, n, counter, ids, gates)
+        s.dispatch(xt, ids)
+        s.expert(s.recv, s.recv, w.expert_mode)
+        s.combine(s.recv, gates, y)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(10):
+        g.replay()
+    torch.cuda.synchronize()
+    counter.zero_()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    ok = int(counter.item()) == steps and int(s.status.item()) == 0
+    out = {"workload": w.describe(), "replays": steps, "us_per_step_with_expert_and_router": round(us, 2),
+           "host_syncs_between_replays": 0, "counter_ok": ok,
+           "algorithmic_bytes_per_step": w.staged_bytes()}
+    s.close()
+    del g
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(np, W, w, sample_tokens):
+    """The CPU oracle as it stands (single-threaded C, fp64) on the same workload with
+    fewer tokens per rank: dispatch + return + combine timed (expert stand-in excluded),
+    reported as effective GB/s over the same staged byte count."""
+    import oracle
+    ws = W.workload(w.name, tokens_per_rank=min(sample_tokens, w.tokens_per_rank))
+    log(f"cpu baseline: oracle on {ws.describe()}")
+    x, ids, gates = W.make_inputs(ws)
+    rows = oracle.as_rows(x)
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        d = oracle.dispatch(rows, ids, ws.experts_per_rank, ws.capacity)
+        t1 = time.perf_counter()
+        R, cap, H = ws.num_ranks, ws.capacity, ws.hidden
+        recv = d["recv"].view(x.dtype).reshape(R, cap, H)
+        z = oracle.expert(recv, d["cnt"], d["recv_off"], ws.experts_per_rank, ws.dtype, ws.expert_mode)
+        t2 = time.perf_counter()
+        ret = oracle.return_exchange(oracle.as_rows(z), d["send_off"], d["recv_off"], ws.tokens_per_rank, ws.top_k)
+        oracle.combine(ret.view(x.dtype).reshape(R, -1, H), d["pos"], gates, ws.dtype)
+        t3 = time.perf_counter()
+        times.append((t1 - t0) + (t3 - t2))
+    t = float(np.median(times))
+    gbps = ws.staged_bytes() / t / 1e9
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "unknown")
+    except OSError:
+        model = "unknown"
+    return {"value": round(gbps, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{ws.describe()} ({ws.tokens_per_rank} of {w.tokens_per_rank} tokens per rank), "
+                      f"median of 3, dispatch+return+combine, {t * 1e3:.0f} ms per step",
+            "host_cpu": model, "host_threads_available": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,319 @@
+// C ABI of the dispatch/combine library (declared in include/a2av.h): argument
+// checks, the handle's workspace, and the launch sequence on the caller's stream.
+// Nothing here reads device data back, synchronises or allocates after a2av_create.
+#include "../../include/a2av.h"
+#include "a2av_internal.h"
+
+#include <new>
+#include <vector>
+
+using a2av::Shape;
+using a2av::Tables;
+
+struct a2av_context {
+    a2av_config_t cfg;
+    Shape sh;
+    int device;
+    void* send_buf;       // [R][T*k][row]: send segments, then the return buffer
+    void* meta;           // tables
+    size_t meta_bytes;
+    Tables tb;
+    bool routed;          // latest planning came from a2av_dispatch (combine allowed)
+    // stage timing
+    std::vector<hipEvent_t> ev;      // per timed call: dispatch 4, combine 3 events
+    int32_t timing_max;
+    int32_t timed_dispatch;
+    int32_t timed_combine;
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int nbits_for(int32_t E) {
+    int b = 0;
+    while ((1ll << b) < E) ++b;
+    return b;
+}
+
+bool make_shape(const a2av_config_t* c, Shape* sh) {
+    if (!c) return false;
+    if (c->num_ranks < 1 || c->num_ranks > a2av::kMaxRanks) return false;
+    if (c->tokens_per_rank < 0 || c->hidden < 1) return false;
+    if (c->dtype != A2AV_F32 && c->dtype != A2AV_BF16) return false;
+    if (c->experts_per_rank < 1) return false;
+    const int64_t E = (int64_t)c->num_ranks * c->experts_per_rank;
+    if (E > a2av::kMaxExperts) return false;
+    if (c->top_k < 1 || c->top_k > a2av::kMaxTopK || c->top_k > E) return false;
+    const int64_t TK = (int64_t)c->tokens_per_rank * c->top_k;
+    if ((int64_t)c->num_ranks * TK > INT32_MAX) return false;          // rows are int32
+    if ((int64_t)c->num_ranks * c->tokens_per_rank > INT32_MAX) return false;
+    if (c->recv_capacity_rows < 0) return false;
+    int64_t cap = c->recv_capacity_rows;
+    if (cap == 0) cap = (int64_t)c->num_ranks * c->tokens_per_rank * std::min<int64_t>(c->top_k, c->experts_per_rank);
+    if (cap > INT32_MAX) return false;
+    sh->R = c->num_ranks;
+    sh->T = c->tokens_per_rank;
+    sh->k = c->top_k;
+    sh->E = (int32_t)E;
+    sh->epr = c->experts_per_rank;
+    sh->H = c->hidden;
+    sh->dtype = c->dtype;
+    sh->nbits = nbits_for((int32_t)E);
+    sh->TK = TK;
+    sh->cap = cap;
+    sh->row_bytes = (int64_t)c->hidden * (c->dtype == A2AV_BF16 ? 2 : 4);
+    return true;
+}
+
+struct MetaLayout {
+    size_t pos, cnt, send_off, recv_counts, recv_off, ticket, total;
+};
+
+MetaLayout meta_layout(const Shape& sh) {
+    MetaLayout m{};
+    size_t o = 0;
+    m.pos = o;         o += align_up(sizeof(int32_t) * (size_t)sh.R * (size_t)std::max<int64_t>(sh.TK, 1));
+    m.cnt = o;         o += align_up(sizeof(int32_t) * (size_t)sh.R * sh.E);
+    m.send_off = o;    o += align_up(sizeof(int32_t) * (size_t)sh.R * (sh.R + 1));
+    m.recv_counts = o; o += align_up(sizeof(int32_t) * (size_t)sh.R * sh.R);
+    m.recv_off = o;    o += align_up(sizeof(int32_t) * (size_t)sh.R * (sh.R + 1));
+    m.ticket = o;      o += kAlign;
+    m.total = o;
+    return m;
+}
+
+size_t send_bytes(const Shape& sh) { return (size_t)sh.R * (size_t)sh.TK * (size_t)sh.row_bytes; }
+
+bool on_device(const a2av_context* h) {
+    int dev = -1;
+    return hipGetDevice(&dev) == hipSuccess && dev == h->device;
+}
+
+int min_vec(const Shape& sh) { return sh.dtype == A2AV_F32 ? 4 : 2; }
+
+// Row arrays are empty when there are no tokens; their pointers may then be null.
+bool has_tokens(const Shape& sh) { return sh.T > 0; }
+
+// Timing: event slots of the next dispatch / combine call, or null when not timing.
+hipEvent_t* dispatch_events(a2av_context* h) {
+    if (h->timed_dispatch >= h->timing_max) return nullptr;
+    return &h->ev[(size_t)h->timed_dispatch++ * 7];
+}
+hipEvent_t* combine_events(a2av_context* h) {
+    if (h->timed_combine >= h->timing_max) return nullptr;
+    return &h->ev[(size_t)h->timed_combine++ * 7 + 4];
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* a2av_error_string(int code) {
+    switch (code) {
+        case A2AV_OK: return "ok";
+        case A2AV_ERR_INVALID: return "invalid argument or configuration";
+        case A2AV_ERR_NOMEM: return "device allocation failed";
+        case A2AV_ERR_HIP: return "HIP runtime error";
+        default: return "unknown error code";
+    }
+}
+
+int64_t a2av_workspace_bytes(const a2av_config_t* cfg) {
+    Shape sh;
+    if (!make_shape(cfg, &sh)) return -1;
+    return (int64_t)(align_up(send_bytes(sh)) + meta_layout(sh).total);
+}
+
+int a2av_create(const a2av_config_t* cfg, a2av_handle_t* out) {
+    if (!out) return A2AV_ERR_INVALID;
+    *out = nullptr;
+    Shape sh;
+    if (!make_shape(cfg, &sh)) return A2AV_ERR_INVALID;
+    a2av_context* h = new (std::nothrow) a2av_context();
+    if (!h) return A2AV_ERR_NOMEM;
+    h->cfg = *cfg;
+    h->sh = sh;
+    if (hipGetDevice(&h->device) != hipSuccess) { delete h; return A2AV_ERR_HIP; }
+    const MetaLayout m = meta_layout(sh);
+    const size_t sb = std::max<size_t>(send_bytes(sh), kAlign);
+    if (hipMalloc(&h->send_buf, sb) != hipSuccess) { (void)hipGetLastError(); delete h; return A2AV_ERR_NOMEM; }
+    if (hipMalloc(&h->meta, m.total) != hipSuccess) {
+        (void)hipGetLastError();
+        (void)hipFree(h->send_buf);
+        delete h;
+        return A2AV_ERR_NOMEM;
+    }
+    h->meta_bytes = m.total;
+    char* b = static_cast<char*>(h->meta);
+    h->tb.pos = reinterpret_cast<int32_t*>(b + m.pos);
+    h->tb.cnt = reinterpret_cast<int32_t*>(b + m.cnt);
+    h->tb.send_off = reinterpret_cast<int32_t*>(b + m.send_off);
+    h->tb.recv_counts = reinterpret_cast<int32_t*>(b + m.recv_counts);
+    h->tb.recv_off = reinterpret_cast<int32_t*>(b + m.recv_off);
+    h->tb.ticket = reinterpret_cast<uint32_t*>(b + m.ticket);
+    // tables start at zero (a combine before any dispatch moves nothing) and so does
+    // the planning grid's arrival ticket
+    if (hipMemset(h->meta, 0, m.total) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+        (void)hipFree(h->meta);
+        (void)hipFree(h->send_buf);
+        delete h;
+        return A2AV_ERR_HIP;
+    }
+    h->routed = false;
+    h->timing_max = 0;
+    h->timed_dispatch = h->timed_combine = 0;
+    *out = h;
+    return A2AV_OK;
+}
+
+int a2av_destroy(a2av_handle_t h) {
+    if (!h) return A2AV_OK;
+    int rc = A2AV_OK;
+    for (hipEvent_t e : h->ev)
+        if (hipEventDestroy(e) != hipSuccess) rc = A2AV_ERR_HIP;
+    if (hipFree(h->meta) != hipSuccess) rc = A2AV_ERR_HIP;
+    if (hipFree(h->send_buf) != hipSuccess) rc = A2AV_ERR_HIP;
+    delete h;
+    return rc;
+}
+
+int a2av_dispatch(a2av_handle_t h, const void* x, const int32_t* topk_ids, void* recv, int32_t* split,
+                  int32_t* recv_counts, int32_t* recv_offsets, uint32_t* status, void* stream) {
+    if (!h || !status || !on_device(h)) return A2AV_ERR_INVALID;
+    const Shape& sh = h->sh;
+    if (has_tokens(sh) && (!x || !topk_ids || (sh.cap > 0 && !recv))) return A2AV_ERR_INVALID;
+    const void* ptrs[] = {x, recv, h->send_buf};
+    const int vec = a2av::pick_vec_bytes(sh.row_bytes, ptrs, 3);
+    if (vec < min_vec(sh)) return A2AV_ERR_INVALID;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipEvent_t* ev = dispatch_events(h);
+    a2av::Outputs out{split, recv_counts, recv_offsets};
+    if (ev && hipEventRecord(ev[0], st) != hipSuccess) return A2AV_ERR_HIP;
+    if (a2av::launch_plan(sh, h->tb, topk_ids, out, status, st) != hipSuccess) return A2AV_ERR_HIP;
+    if (ev && hipEventRecord(ev[1], st) != hipSuccess) return A2AV_ERR_HIP;
+    if (a2av::launch_pack(sh, h->tb, x, h->send_buf, vec, st) != hipSuccess) return A2AV_ERR_HIP;
+    if (ev && hipEventRecord(ev[2], st) != hipSuccess) return A2AV_ERR_HIP;
+    if (a2av::launch_exchange(sh, h->tb, h->send_buf, recv, false, vec, st) != hipSuccess) return A2AV_ERR_HIP;
+    if (ev && hipEventRecord(ev[3], st) != hipSuccess) return A2AV_ERR_HIP;
+    h->routed = true;
+    return A2AV_OK;
+}
+
+int a2av_combine(a2av_handle_t h, const void* expert_out, const float* gates, void* y, uint32_t* status,
+                 void* stream) {
+    if (!h || !status || !on_device(h) || !h->routed) return A2AV_ERR_INVALID;
+    const Shape& sh = h->sh;
+    if (has_tokens(sh) && (!gates || !y || (sh.cap > 0 && !expert_out))) return A2AV_ERR_INVALID;
+    const void* ptrs[] = {expert_out, y, h->send_buf};
+    const int vec = a2av::pick_vec_bytes(sh.row_bytes, ptrs, 3);
+    if (vec < min_vec(sh) || ((uintptr_t)gates % 4) != 0) return A2AV_ERR_INVALID;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipEvent_t* ev = combine_events(h);
+    if (ev && hipEventRecord(ev[0], st) != hipSuccess) return A2AV_ERR_HIP;
+    if (a2av::launch_exchange(sh, h->tb, expert_out, h->send_buf, true, vec, st) != hipSuccess) return A2AV_ERR_HIP;
+    if (ev && hipEventRecord(ev[1], st) != hipSuccess) return A2AV_ERR_HIP;
+    if (a2av::launch_combine(sh, h->tb, h->send_buf, gates, y, vec, st) != hipSuccess) return A2AV_ERR_HIP;
+    if (ev && hipEventRecord(ev[2], st) != hipSuccess) return A2AV_ERR_HIP;
+    return A2AV_OK;
+}
+
+int a2av_alltoallv(a2av_handle_t h, const void* send, const int32_t* send_counts, void* recv, int32_t* recv_counts,
+                   int32_t* recv_offsets, uint32_t* status, void* stream) {
+    if (!h || !send_counts || !status || !on_device(h)) return A2AV_ERR_INVALID;
+    const Shape& sh = h->sh;
+    if (has_tokens(sh) && (!send || (sh.cap > 0 && !recv))) return A2AV_ERR_INVALID;
+    const void* ptrs[] = {send, recv};
+    const int vec = a2av::pick_vec_bytes(sh.row_bytes, ptrs, 2);
+    if (vec < min_vec(sh)) return A2AV_ERR_INVALID;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    h->routed = false;
+    a2av::Outputs out{nullptr, recv_counts, recv_offsets};
+    if (a2av::launch_plan_from_counts(sh, h->tb, send_counts, out, status, st) != hipSuccess) return A2AV_ERR_HIP;
+    if (a2av::launch_exchange(sh, h->tb, send, recv, false, vec, st) != hipSuccess) return A2AV_ERR_HIP;
+    return A2AV_OK;
+}
+
+int a2av_copy_positions(a2av_handle_t h, int32_t* pos, void* stream) {
+    if (!h || !on_device(h)) return A2AV_ERR_INVALID;
+    const size_t n = sizeof(int32_t) * (size_t)h->sh.R * (size_t)h->sh.TK;
+    if (n == 0) return A2AV_OK;
+    if (!pos) return A2AV_ERR_INVALID;
+    return hipMemcpyAsync(pos, h->tb.pos, n, hipMemcpyDeviceToDevice, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? A2AV_OK : A2AV_ERR_HIP;
+}
+
+int a2av_copy_send_offsets(a2av_handle_t h, int32_t* send_offsets, void* stream) {
+    if (!h || !send_offsets || !on_device(h)) return A2AV_ERR_INVALID;
+    const size_t n = sizeof(int32_t) * (size_t)h->sh.R * (h->sh.R + 1);
+    return hipMemcpyAsync(send_offsets, h->tb.send_off, n, hipMemcpyDeviceToDevice,
+                          static_cast<hipStream_t>(stream)) == hipSuccess ? A2AV_OK : A2AV_ERR_HIP;
+}
+
+int a2av_expert_apply(a2av_handle_t h, const void* in, void* out, int32_t mode, void* stream) {
+    if (!h || !on_device(h) || !h->routed) return A2AV_ERR_INVALID;
+    if (mode != A2AV_EXPERT_IDENTITY && mode != A2AV_EXPERT_SCALE) return A2AV_ERR_INVALID;
+    const Shape& sh = h->sh;
+    if (has_tokens(sh) && sh.cap > 0 && (!in || !out)) return A2AV_ERR_INVALID;
+    const void* ptrs[] = {in, out};
+    const int vec = a2av::pick_vec_bytes(sh.row_bytes, ptrs, 2);
+    if (vec < min_vec(sh)) return A2AV_ERR_INVALID;
+    return a2av::launch_expert(sh, h->tb, in, out, mode, vec, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? A2AV_OK : A2AV_ERR_HIP;
+}
+
+int a2av_route_step(const int32_t* ids_table, const float* gates_table, int32_t steps, int64_t n, int32_t* counter,
+                    int32_t* ids, float* gates, void* stream) {
+    if (!ids_table || !gates_table || !counter || !ids || !gates || steps < 1 || n < 0) return A2AV_ERR_INVALID;
+    return a2av::launch_route_step(ids_table, gates_table, steps, n, counter, ids, gates,
+                                   static_cast<hipStream_t>(stream)) == hipSuccess ? A2AV_OK : A2AV_ERR_HIP;
+}
+
+int a2av_timing_begin(a2av_handle_t h, int32_t max_calls) {
+    if (!h || max_calls < 1) return A2AV_ERR_INVALID;
+    for (hipEvent_t e : h->ev) (void)hipEventDestroy(e);
+    h->ev.assign((size_t)max_calls * 7, nullptr);
+    for (auto& e : h->ev)
+        if (hipEventCreate(&e) != hipSuccess) {
+            h->timing_max = 0;
+            return A2AV_ERR_HIP;
+        }
+    h->timing_max = max_calls;
+    h->timed_dispatch = h->timed_combine = 0;
+    return A2AV_OK;
+}
+
+int a2av_timing_end(a2av_handle_t h, double* ms_sum, int32_t* launches) {
+    if (!h || !ms_sum || !launches) return A2AV_ERR_INVALID;
+    for (int i = 0; i < A2AV_STAGES; ++i) { ms_sum[i] = 0.0; launches[i] = 0; }
+    int rc = A2AV_OK;
+    auto add = [&](hipEvent_t a, hipEvent_t b, int stage) {
+        float ms = 0.0f;
+        if (hipEventSynchronize(b) != hipSuccess || hipEventElapsedTime(&ms, a, b) != hipSuccess) {
+            rc = A2AV_ERR_HIP;
+            return;
+        }
+        ms_sum[stage] += ms;
+        launches[stage] += 1;
+    };
+    for (int32_t c = 0; c < h->timed_dispatch; ++c) {
+        hipEvent_t* e = &h->ev[(size_t)c * 7];
+        add(e[0], e[1], 0);
+        add(e[1], e[2], 1);
+        add(e[2], e[3], 2);
+    }
+    for (int32_t c = 0; c < h->timed_combine; ++c) {
+        hipEvent_t* e = &h->ev[(size_t)c * 7 + 4];
+        add(e[0], e[1], 3);
+        add(e[1], e[2], 4);
+    }
+    for (hipEvent_t e : h->ev) (void)hipEventDestroy(e);
+    h->ev.clear();
+    h->timing_max = 0;
+    h->timed_dispatch = h->timed_combine = 0;
+    return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,68 @@
+// Internal declarations shared by the C-ABI host code and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace a2av {
+
+// Problem shape, fixed at handle creation.
+struct Shape {
+    int32_t R;          // virtual ranks
+    int32_t T;          // tokens per rank
+    int32_t k;          // top-k
+    int32_t E;          // experts
+    int32_t epr;        // experts per rank
+    int32_t H;          // elements per row
+    int32_t dtype;      // 0 f32, 1 bf16
+    int32_t nbits;      // bits needed to tell experts apart: ceil(log2(E))
+    int64_t TK;         // T * k, send rows per rank
+    int64_t cap;        // receive rows per rank
+    int64_t row_bytes;  // H * element bytes
+};
+
+// Device tables in the handle's workspace (rank-major, int32 rows).
+struct Tables {
+    int32_t* pos;          // [R][TK]   place of each (token, slot) in its rank's send order, -1 dropped
+    int32_t* cnt;          // [R][E]    rows per (source rank, expert)
+    int32_t* send_off;     // [R][R+1]  segment starts in each send buffer
+    int32_t* recv_counts;  // [R][R]    [dst][src]
+    int32_t* recv_off;     // [R][R+1]  [dst][src] exclusive prefix over src
+    uint32_t* ticket;      // arrival counter of the planning grid (reset by its last block)
+};
+
+// Optional copies of the tables for the caller (any may be null).
+struct Outputs {
+    int32_t* split;
+    int32_t* recv_counts;
+    int32_t* recv_off;
+};
+
+// Byte width of the vector used for row copies: the largest of 16, 8, 4, 2 dividing
+// the row size and the alignment of every base address involved.
+int pick_vec_bytes(int64_t row_bytes, const void* const* ptrs, int nptrs);
+
+hipError_t launch_plan(const Shape& sh, const Tables& tb, const int32_t* ids, const Outputs& out,
+                       uint32_t* status, hipStream_t st);
+hipError_t launch_plan_from_counts(const Shape& sh, const Tables& tb, const int32_t* send_counts,
+                                   const Outputs& out, uint32_t* status, hipStream_t st);
+hipError_t launch_pack(const Shape& sh, const Tables& tb, const void* x, void* send, int vec,
+                       hipStream_t st);
+hipError_t launch_exchange(const Shape& sh, const Tables& tb, const void* src, void* dst, bool reverse,
+                           int vec, hipStream_t st);
+hipError_t launch_combine(const Shape& sh, const Tables& tb, const void* ret, const float* gates, void* y,
+                          int vec, hipStream_t st);
+hipError_t launch_expert(const Shape& sh, const Tables& tb, const void* in, void* out, int mode, int vec,
+                         hipStream_t st);
+hipError_t launch_route_step(const int32_t* ids_table, const float* gates_table, int32_t steps, int64_t n,
+                             int32_t* counter, int32_t* ids, float* gates, hipStream_t st);
+
+// Dynamic LDS the planning kernel may use, and so the largest expert count: two rows
+// of E counters (one wavefront's and the totals) must fit.
+constexpr int32_t kPlanLdsBytes = 63 * 1024;
+constexpr int32_t kMaxExperts = 4096;
+static_assert(2 * 4 * kMaxExperts <= kPlanLdsBytes, "planning LDS budget");
+constexpr int32_t kMaxRanks = 1024;
+constexpr int32_t kMaxTopK = 64;
+
+}  // namespace a2av

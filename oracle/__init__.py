@@ -146,21 +146,27 @@ def combine(ret: np.ndarray, pos: np.ndarray, gates: np.ndarray, dtype: int) -> 
 
 def closed_form(x: np.ndarray, ids: np.ndarray, gates: np.ndarray, experts_per_rank: int, dtype: int,
                 mode: int, tok_begin: int = 0, tok_end=None) -> np.ndarray:
-    """Layout-free end result y[s][t] = RNE(sum_j g * f_e(x[s][t])) for tokens [tok_begin, tok_end)."""
+    """Layout-free end result y[s][t] = RNE(sum_j g * f_e(x[s][t])).
+
+    Computes the tokens [tok_begin, tok_end) of the flattened [R*T] range and returns
+    them as an array of shape [tok_end - tok_begin][H] (the full [R][T][H] when the
+    whole range is asked for)."""
     x = np.ascontiguousarray(x)
     ids = _c(ids, np.int32)
     gates = _c(gates, np.float32)
     R, T, k = ids.shape
     H = x.shape[2]
     N = R * T
+    whole = tok_begin == 0 and (tok_end is None or tok_end == N)
     if tok_end is None:
         tok_end = N
-    y = np.zeros_like(x)
+    tok_begin, tok_end = max(0, tok_begin), min(N, tok_end)
+    y = np.zeros((max(0, tok_end - tok_begin), H), x.dtype)
     rc = _load().oracle_closed_form(R, T, k, experts_per_rank, H, dtype, mode, _p(x), _p(ids), _p(gates),
                                     _p(y), tok_begin, tok_end)
     if rc != 0:
         raise ValueError("oracle_closed_form rejected its arguments")
-    return y
+    return y.reshape(R, T, H) if whole else y
 
 
 def full_step(x: np.ndarray, ids: np.ndarray, gates: np.ndarray, experts_per_rank: int, dtype: int,

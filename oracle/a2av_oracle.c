@@ -315,7 +315,7 @@ int oracle_combine(int32_t R, int32_t T, int32_t k, int64_t H, int32_t dtype,
  * sum.  The combine does not depend on how rows were placed in between, so this is a
  * second, independent formulation of dispatch -> expert -> return -> combine when no
  * row is dropped for capacity.  Tokens [tok_begin, tok_end) of the flattened [R*T]
- * range are computed; y is indexed globally.
+ * range are computed; y holds their rows only (row 0 of y is token tok_begin).
  * ------------------------------------------------------------------------------- */
 int oracle_closed_form(int32_t R, int32_t T, int32_t k, int32_t epr, int64_t H, int32_t dtype,
                        int32_t mode, const uint8_t* x, const int32_t* ids, const float* gates,
@@ -329,7 +329,7 @@ int oracle_closed_form(int32_t R, int32_t T, int32_t k, int32_t epr, int64_t H, 
     if (tok_end > N) tok_end = N;
     for (int64_t n = tok_begin; n < tok_end; ++n) {
         const uint8_t* in = x + n * rb;
-        uint8_t* out = y + n * rb;
+        uint8_t* out = y + (n - tok_begin) * rb;
         for (int64_t h = 0; h < H; ++h) {
             double v = load_elem(in, h, dtype);
             double acc = 0.0;

@@ -1,0 +1,56 @@
+"""The C-ABI library loads and exports every entry point include/a2av.h declares; host-only
+calls (no GPU work) behave as documented.  Runs without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from moe_alltoallv_resident_amd import a2av
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "a2av.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(a2av_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_documented_entry_points():
+    names = declared_functions()
+    for required in ("a2av_create", "a2av_dispatch", "a2av_combine", "a2av_destroy"):
+        assert required in names
+    assert set(names) == set(a2av.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = a2av.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_error_strings():
+    assert a2av.error_string(a2av.OK) == "ok"
+    assert "invalid" in a2av.error_string(a2av.ERR_INVALID)
+    assert "unknown" in a2av.error_string(12345)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(num_ranks=0), dict(num_ranks=2000), dict(tokens_per_rank=-1), dict(hidden=0), dict(dtype=7),
+    dict(experts_per_rank=0), dict(experts_per_rank=513), dict(top_k=0), dict(top_k=65),
+    dict(num_ranks=2, experts_per_rank=1, top_k=3), dict(recv_capacity_rows=-5),
+])
+def test_workspace_bytes_rejects_invalid_configs(bad):
+    base = dict(num_ranks=8, tokens_per_rank=128, hidden=5120, dtype=a2av.BF16, experts_per_rank=16, top_k=1)
+    base.update(bad)
+    assert a2av.a2av_workspace_bytes(a2av.make_config(**base)) == -1
+
+
+def test_workspace_bytes_counts_send_buffer_and_tables():
+    R, T, H, epr, k = 8, 8192, 5120, 16, 1
+    n = a2av.a2av_workspace_bytes(a2av.make_config(R, T, H, a2av.BF16, epr, k))
+    send = R * T * k * H * 2
+    assert send < n < send + 4 * 1024 * 1024

@@ -1,0 +1,161 @@
+"""Error paths of the C ABI.  Host-detectable problems return A2AV_ERR_INVALID and enqueue
+nothing; problems only the GPU sees (expert ids out of range, a receive slice too small)
+set status bits and never write out of bounds: guard rows around the receive buffer keep
+their pattern.  All conditions are forced from the host; every kernel exits normally."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from moe_alltoallv_resident_amd import a2av
+from moe_alltoallv_resident_amd import workloads as W
+from tests.gpu_util import assert_combine_close, banner, host_bits, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _cfg(w):
+    return a2av.make_config(w.num_ranks, w.tokens_per_rank, w.hidden, w.dtype, w.experts_per_rank, w.top_k,
+                            w.recv_capacity_rows)
+
+
+def test_host_side_rejections_enqueue_nothing():
+    w = W.workload("tiny")
+    x, ids, gates = W.make_inputs(w)
+    xt, idt, gt = to_device(w, x, ids, gates)
+    h = a2av.a2av_create(_cfg(w))
+    L = a2av.lib()
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    recv = torch.empty((w.num_ranks, w.capacity, w.hidden), dtype=torch.float32, device="cuda")
+    y = torch.empty_like(xt)
+    vp = ctypes.c_void_p
+    P = lambda t: vp(t.data_ptr())  # noqa: E731
+    null = vp(0)
+    stream = vp(torch.cuda.current_stream().cuda_stream)
+    # combine before any dispatch
+    assert L.a2av_combine(h, P(recv), P(gt), P(y), P(st), stream) == a2av.ERR_INVALID
+    # null required pointers
+    assert L.a2av_dispatch(h, null, P(idt), P(recv), None, None, None, P(st), stream) == a2av.ERR_INVALID
+    assert L.a2av_dispatch(h, P(xt), null, P(recv), None, None, None, P(st), stream) == a2av.ERR_INVALID
+    assert L.a2av_dispatch(h, P(xt), P(idt), null, None, None, None, P(st), stream) == a2av.ERR_INVALID
+    assert L.a2av_dispatch(h, P(xt), P(idt), P(recv), None, None, None, null, stream) == a2av.ERR_INVALID
+    # misaligned row data (float32 rows need 4-byte alignment)
+    assert L.a2av_dispatch(h, vp(xt.data_ptr() + 2), P(idt), P(recv), None, None, None, P(st),
+                           stream) == a2av.ERR_INVALID
+    # bad expert stand-in mode
+    a2av.a2av_dispatch(h, xt, idt, recv, None, None, None, st)
+    assert L.a2av_expert_apply(h, P(recv), P(recv), 7, stream) == a2av.ERR_INVALID
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    a2av.a2av_destroy(h)
+    # invalid configuration
+    bad = _cfg(w)
+    bad.top_k = 99
+    with pytest.raises(a2av.A2AVError):
+        a2av.a2av_create(bad)
+
+
+def test_receive_overflow_keeps_guard_rows_and_true_counts():
+    w = W.workload("wide", num_ranks=4, tokens_per_rank=64, hidden=96, experts_per_rank=2, top_k=2)
+    x, ids, gates = W.make_inputs(w)
+    full = oracle.dispatch(oracle.as_rows(x), ids, w.experts_per_rank, w.capacity)
+    cap = int(full["recv_off"][:, w.num_ranks].max()) - 7
+    w = W.workload("wide", num_ranks=4, tokens_per_rank=64, hidden=96, experts_per_rank=2, top_k=2,
+                   recv_capacity_rows=cap)
+    banner(f"overflow: cap {cap} rows per rank")
+    xt, idt, gt = to_device(w, x, ids, gates)
+    guard = 5
+    R = w.num_ranks
+    big = torch.full((R * cap + 2 * guard, w.hidden), -7.0, dtype=torch.bfloat16, device="cuda")
+    recv = big[guard:guard + R * cap].view(R, cap, w.hidden)
+    split = torch.empty((R, w.num_experts), dtype=torch.int32, device="cuda")
+    rc = torch.empty((R, R), dtype=torch.int32, device="cuda")
+    ro = torch.empty((R, R + 1), dtype=torch.int32, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    h = a2av.a2av_create(_cfg(w))
+    a2av.a2av_dispatch(h, xt, idt, recv, split, rc, ro, st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == a2av.ST_RECV_OVERFLOW
+    ref = oracle.dispatch(oracle.as_rows(x), ids, w.experts_per_rank, cap)
+    assert ref["status"] == oracle.ST_RECV_OVERFLOW
+    assert np.array_equal(host_bits(rc), ref["recv_counts"])
+    assert np.array_equal(host_bits(ro), ref["recv_off"])
+    got = host_bits(recv)
+    want = ref["recv"].view(np.uint16).reshape(R, cap, w.hidden)
+    for d in range(R):
+        n = min(int(ref["recv_off"][d, R]), cap)
+        assert np.array_equal(got[d, :n], want[d, :n])
+        assert np.all(got[d, n:] == np.uint16(0xC0E0)), "rows past the received count were written"
+    g = host_bits(big)
+    assert np.all(g[:guard] == np.uint16(0xC0E0)) and np.all(g[-guard:] == np.uint16(0xC0E0))
+    # combine: dropped rows add nothing, as in the oracle
+    y = torch.empty_like(xt)
+    a2av.a2av_expert_apply(h, recv, recv, a2av.EXPERT_SCALE)
+    a2av.a2av_combine(h, recv, gt, y, st)
+    torch.cuda.synchronize()
+    oref = oracle.full_step(x, ids, gates, w.experts_per_rank, w.dtype, w.expert_mode, cap)
+    assert_combine_close(host_bits(y), oref["y"], w.dtype, "overflow combine")
+    a2av.a2av_destroy(h)
+
+
+def test_bare_alltoallv_matches_oracle_exchange():
+    """a2av_alltoallv on pre-sorted send buffers and device counts equals the oracle's
+    exchange of the same rows (ids chosen so that the sort is the identity)."""
+    R, T, H = 6, 40, 64
+    rng = np.random.default_rng(4)
+    dest = np.sort(rng.integers(0, R, size=(R, T)), axis=1).astype(np.int32)   # sorted per sender
+    dest[2] = 0                                                                 # one sender, one peer
+    dest[4, :] = np.sort(rng.integers(3, 5, size=T))                             # zero-length segments
+    w = W.Workload("bare", R, T, H, W.BF16, 1, 1, "uniform", "softmax", 0)
+    x = W.make_x(w)
+    ref = oracle.dispatch(oracle.as_rows(x), dest[..., None], 1, w.capacity)
+    send_counts = np.stack([np.bincount(dest[s], minlength=R) for s in range(R)]).astype(np.int32)
+    xt, _, _ = to_device(w, x, dest[..., None], np.ones((R, T, 1), np.float32))
+    h = a2av.a2av_create(_cfg(w))
+    recv = torch.empty((R, w.capacity, H), dtype=torch.bfloat16, device="cuda")
+    rc = torch.empty((R, R), dtype=torch.int32, device="cuda")
+    ro = torch.empty((R, R + 1), dtype=torch.int32, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sc = torch.from_numpy(send_counts).cuda()
+    a2av.a2av_alltoallv(h, xt, sc, recv, rc, ro, st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert np.array_equal(host_bits(rc), ref["recv_counts"])
+    assert np.array_equal(host_bits(ro), ref["recv_off"])
+    got = host_bits(recv)
+    want = ref["recv"].view(np.uint16).reshape(R, w.capacity, H)
+    for d in range(R):
+        n = int(ref["recv_off"][d, R])
+        assert np.array_equal(got[d, :n], want[d, :n])
+    # combine is refused after the bare collective
+    y = torch.empty_like(xt)
+    with pytest.raises(a2av.A2AVError):
+        a2av.a2av_combine(h, recv, torch.ones((R, T, 1), device="cuda"), y, st)
+    # bad counts: a negative count and a sender over its rows are flagged and sent as 0
+    bad = send_counts.copy()
+    bad[1, 0] = -1
+    bad[3, 2] += T
+    st.zero_()
+    a2av.a2av_alltoallv(h, xt, torch.from_numpy(bad).cuda(), recv, rc, ro, st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == a2av.ST_EXPERT_RANGE
+    rch = host_bits(rc)
+    assert np.all(rch[:, 1] == 0) and np.all(rch[:, 3] == 0)
+    a2av.a2av_destroy(h)
+
+
+def test_zero_tokens():
+    w = W.workload("decode", tokens_per_rank=0)
+    h = a2av.a2av_create(_cfg(w))
+    R = w.num_ranks
+    split = torch.full((R, w.num_experts), 5, dtype=torch.int32, device="cuda")
+    rc = torch.full((R, R), 5, dtype=torch.int32, device="cuda")
+    ro = torch.full((R, R + 1), 5, dtype=torch.int32, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    empty = torch.empty(0, device="cuda")
+    a2av.a2av_dispatch(h, empty, empty, empty, split, rc, ro, st)
+    torch.cuda.synchronize()
+    assert not split.any() and not rc.any() and not ro.any() and int(st.item()) == 0
+    a2av.a2av_destroy(h)

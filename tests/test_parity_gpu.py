@@ -1,0 +1,193 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Small and ragged cases: every output element by element against the oracle's staged path
+(tables, positions, receive rows and expert rows bit-exact; the combine within the
+tolerance in tests/gpu_util.py).  The five workloads at their full sizes, in the launch
+configuration bench.py times: every table, every position and every receive row
+bit-exact (the oracle routes 4-byte tags, row content not entering the routing, and each
+GPU receive row must equal the input row its tag names), the combine against the
+oracle's closed form on sampled token ranges plus a float32 torch evaluation of the same
+definition on every token.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from moe_alltoallv_resident_amd import a2av
+from moe_alltoallv_resident_amd import workloads as W
+from tests.gpu_util import (Run, assert_combine_close, assert_tables_equal, banner, host_bits,
+                            oracle_tables)
+
+pytestmark = pytest.mark.gpu
+
+
+def _free():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _full_oracle_check(w: W.Workload, x, ids, gates, run: Run = None):
+    banner(f"full check {w.describe()} cap={w.capacity}")
+    ref = oracle.full_step(x, ids, gates, w.experts_per_rank, w.dtype, w.expert_mode, w.capacity)
+    run = run or Run(w, x, ids, gates).all()
+    R = w.num_ranks
+    assert_tables_equal(run, ref, R)
+    assert run.status == ref["status"], (run.status, ref["status"])
+    for d in range(R):
+        n = run.valid[d]
+        assert np.array_equal(run.recv[d], ref["recv"][d, :n]), f"recv rows of rank {d}"
+        assert np.array_equal(run.z[d], ref["z"][d, :n]), f"expert rows of rank {d}"
+    exact = assert_combine_close(run.y, ref["y"], w.dtype, w.describe())
+    banner(f"  combine bit-identical fraction {exact:.6f}")
+    session = run.session
+    del run
+    session.close()
+    _free()
+    return ref
+
+
+# -------------------------------------------------------------- small / ragged cases
+
+SMALL = [
+    ("tiny", {}),
+    ("decode", {}),
+    ("edge", {}),
+    ("prefill", dict(tokens_per_rank=300, hidden=512)),
+    ("wide", dict(tokens_per_rank=40, hidden=256)),
+    # one rank talking to itself, row not a multiple of 64 vectors
+    ("wide", dict(num_ranks=1, tokens_per_rank=37, hidden=1000, experts_per_rank=8, top_k=3)),
+    # rows of 198 bytes: 2-byte vectors
+    ("wide", dict(num_ranks=5, tokens_per_rank=13, hidden=99, experts_per_rank=3, top_k=3)),
+    # rows of 200 bytes: 8-byte vectors
+    ("wide", dict(num_ranks=3, tokens_per_rank=29, hidden=100, experts_per_rank=4, top_k=2)),
+    # float32 rows of 132 bytes: 4-byte vectors, scaled experts
+    ("tiny", dict(num_ranks=6, tokens_per_rank=21, hidden=33, experts_per_rank=2, top_k=4,
+                  expert_mode=W.EXPERT_SCALE)),
+    # every expert chosen by every token (k = E)
+    ("tiny", dict(num_ranks=2, tokens_per_rank=9, hidden=64, experts_per_rank=2, top_k=4)),
+    # no tokens at all
+    ("decode", dict(tokens_per_rank=0)),
+    # many ranks, one expert each
+    ("edge", dict(num_ranks=64, tokens_per_rank=3, hidden=64)),
+    # largest expert count held in LDS (4096 experts, two wavefronts per planning block)
+    ("wide", dict(num_ranks=8, tokens_per_rank=64, hidden=64, experts_per_rank=512, top_k=4)),
+    # largest top-k
+    ("wide", dict(num_ranks=4, tokens_per_rank=5, hidden=64, experts_per_rank=32, top_k=64)),
+    # largest rank count
+    ("edge", dict(num_ranks=1024, tokens_per_rank=2, hidden=16, routing="uniform")),
+    # long runs per wavefront: 8192 assignments per rank spread over 16 wavefronts
+    ("decode", dict(num_ranks=2, tokens_per_rank=8192, hidden=8)),
+    # a small receive capacity (rows dropped, flagged, counts kept)
+    ("wide", dict(num_ranks=4, tokens_per_rank=30, hidden=64, experts_per_rank=2, top_k=2,
+                  recv_capacity_rows=20)),
+]
+
+
+@pytest.mark.parametrize("name,over", SMALL, ids=[f"{n}-{i}" for i, (n, _) in enumerate(SMALL)])
+def test_small_and_ragged_cases_match_oracle(name, over):
+    w = W.workload(name, **over)
+    x, ids, gates = W.make_inputs(w)
+    ref = _full_oracle_check(w, x, ids, gates)
+    if over.get("recv_capacity_rows"):
+        assert ref["status"] & oracle.ST_RECV_OVERFLOW
+
+
+def test_repeated_ids_within_a_token_are_sent_k_times():
+    w = W.workload("tiny", num_ranks=3, tokens_per_rank=50, hidden=32, experts_per_rank=2, top_k=3)
+    x, _, gates = W.make_inputs(w)
+    ids = np.random.default_rng(9).integers(0, w.num_experts, size=(3, 50, 3)).astype(np.int32)
+    _full_oracle_check(w, x, ids, gates)
+
+
+def test_out_of_range_ids_are_dropped_and_flagged():
+    w = W.workload("wide", num_ranks=4, tokens_per_rank=24, hidden=128, experts_per_rank=4, top_k=2)
+    x, ids, gates = W.make_inputs(w)
+    ids = ids.copy()
+    ids[0, 3, 1] = w.num_experts
+    ids[2, 0, 0] = -1
+    ids[3, 23, 1] = 1 << 30
+    ref = _full_oracle_check(w, x, ids, gates)
+    assert ref["status"] == oracle.ST_EXPERT_RANGE
+
+
+def test_decode_steps_with_fresh_routing():
+    w = W.workload("decode")
+    x = W.make_x(w)
+    session = a2av.Session(w.num_ranks, w.tokens_per_rank, w.hidden, w.dtype, w.experts_per_rank, w.top_k)
+    for step in range(3):
+        ids, gates = W.make_ids(w, step), W.make_gates(w, step)
+        run = Run(w, x, ids, gates, session=session).all()
+        ref = oracle.full_step(x, ids, gates, w.experts_per_rank, w.dtype, w.expert_mode, w.capacity)
+        assert_tables_equal(run, ref, w.num_ranks)
+        assert_combine_close(run.y, ref["y"], w.dtype, f"decode step {step}")
+    session.close()
+    _free()
+
+
+# ------------------------------------------------------------ full-size workloads
+
+def _torch_definition_f32(w: W.Workload, x_dev, ids_dev, gates_dev, chunk=4096):
+    """y = sum_j g_j * round(x * (1 + e_j/256)) evaluated by torch in float32 (a property
+    check at full size: same definition, float32 accumulation in slot order)."""
+    N, k = w.tokens, w.top_k
+    xf = x_dev.reshape(N, w.hidden)
+    idsf = ids_dev.reshape(N, k)
+    gf = gates_dev.reshape(N, k)
+    out = torch.empty_like(xf)
+    for a in range(0, N, chunk):
+        b = min(N, a + chunk)
+        acc = torch.zeros((b - a, w.hidden), dtype=torch.float32, device=xf.device)
+        for j in range(k):
+            e = idsf[a:b, j].to(torch.float32)
+            z = xf[a:b].float()
+            if w.expert_mode == W.EXPERT_SCALE:
+                z = (z * (1.0 + e / 256.0)[:, None]).to(xf.dtype).float()
+            acc = torch.addcmul(acc, gf[a:b, j:j + 1], z)
+        out[a:b] = acc.to(xf.dtype)
+    return out.reshape(x_dev.shape)
+
+
+@pytest.mark.parametrize("name", ["decode", "prefill", "wide", "edge", "tiny"])
+def test_full_size_workload(name):
+    w = W.workload(name)
+    banner(f"full size {w.describe()} cap={w.capacity}")
+    x, ids, gates = W.make_inputs(w)
+    ref = oracle_tables(w, ids)
+    run = Run(w, x, ids, gates).dispatch(keep_recv=False)
+    assert_tables_equal(run, ref, w.num_ranks)
+    assert run.session.status.item() == 0
+
+    # every receive row equals the input row its oracle tag names
+    s = run.session
+    xf = run.x_dev.reshape(w.tokens, w.hidden)
+    for d in range(w.num_ranks):
+        n = run.valid[d]
+        if n == 0:
+            continue
+        tags = torch.from_numpy(ref["recv_tags"][d, :n].astype(np.int64)).cuda()
+        assert torch.equal(s.recv[d, :n], xf.index_select(0, tags)), f"receive rows of rank {d}"
+    banner("  receive rows bit-exact")
+    run.expert(keep_z=False).combine()
+    assert run.status == 0
+
+    # combine on sampled token ranges against the oracle's closed form
+    rng = np.random.default_rng(17)
+    budget = {"prefill": 4096, "wide": 1024}.get(name, w.tokens)
+    span = min(budget, 256) if budget < w.tokens else w.tokens
+    starts = [0] if span == w.tokens else sorted(
+        set([0, w.tokens - span] + list(rng.integers(0, w.tokens - span, budget // span - 2))))
+    y_host = run.y.reshape(w.tokens, w.hidden)
+    checked = 0
+    for a in starts:
+        yref = oracle.closed_form(x, ids, gates, w.experts_per_rank, w.dtype, w.expert_mode, a, a + span)
+        assert_combine_close(y_host[a:a + span], yref.reshape(span, w.hidden), w.dtype, f"{name} tokens {a}+{span}")
+        checked += span
+    banner(f"  combine matches the oracle on {checked} sampled tokens")
+
+    # every token: the same definition in float32 torch arithmetic
+    yt = _torch_definition_f32(w, run.x_dev, run.ids_dev, run.gates_dev)
+    assert_combine_close(run.y, host_bits(yt), w.dtype, f"{name} torch float32 definition")
+    s.close()
+    del run, s, yt
+    _free()
