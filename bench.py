@@ -31,6 +31,25 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter passes
+    (profiles/hbm_traffic.json: FETCH_SIZE and WRITE_SIZE scaled by a copy kernel of
+    known size), or None when the kernels' source changed since the counters were taken
+    or no counters exist for this workload and kernel."""
+    import hashlib
+    try:
+        with open(os.path.join(ROOT, "profiles", "hbm_traffic.json")) as f:
+            rec = json.load(f)
+        with open(os.path.join(ROOT, "moe_alltoallv_resident_amd", "csrc", "a2av_kernels.hip"), "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != sha or rec.get("workload") != workload:
+        return None
+    b = rec.get("per_launch_bytes", {}).get(kernel)
+    return None if b is None else int(b["read"] + b["write"])
+
+
 def stage_bytes(w):
     """Algorithmic bytes per launch of each stage (real rows only)."""
     N, A, row = w.tokens, w.assignments, w.row_bytes
@@ -52,7 +71,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode-graph", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    ap.add_argument("--profile-summary", nargs="+", metavar="DB",
+                    help="print per-kernel statistics of rocprofv3 database(s) and exit (no GPU)")
     args = ap.parse_args()
+    if args.profile_summary:
+        profile_summary(args.profile_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the R virtual ranks live in one GPU's HBM and no "
               f"collective crosses GPUs, so --gpus {args.gpus} is not supported", file=sys.stderr)
@@ -150,7 +174,8 @@ def main():
         "stage_us": {n: round(v * 1e3, 2) for n, v in stage_ms.items()},
         "roofline": {
             "bound": "hbm", "kernel": dom, "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+            "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": measured_traffic(w.name, dom),
             "bytes_per_launch": sb[dom], "copy_reference_GBps": round(copy_gbps, 1),
         },
     }
@@ -253,6 +278,44 @@ def cpu_baseline(np, W, w, sample_tokens):
             "sample": f"{ws.describe()} ({ws.tokens_per_rank} of {w.tokens_per_rank} tokens per rank), "
                       f"median of 3, dispatch+return+combine, {t * 1e3:.0f} ms per step",
             "host_cpu": model, "host_threads_available": os.cpu_count()}
+
+
+def _short_kernel_name(name):
+    base = name.replace("void ", "").replace("a2av::(anonymous namespace)::", "")
+    base = base.replace("unsigned int __vector(4)", "u32x4").replace("unsigned int __vector(2)", "u32x2")
+    return base.split("(")[0]
+
+
+def profile_summary(paths):
+    """Per (kernel, grid size) statistics from rocprofv3 rocpd databases: launches,
+    average / min / max duration, and the average of every hardware counter collected
+    (FETCH_SIZE / WRITE_SIZE are KiB per dispatch)."""
+    import sqlite3
+    for path in paths:
+        c = sqlite3.connect(path)
+        print(f"# {os.path.basename(path)}")
+        rows = c.execute("select name, grid_x, workgroup_x, duration from kernels").fetchall()
+        groups = {}
+        for name, gx, wx, dur in rows:
+            groups.setdefault((_short_kernel_name(name), gx, wx), []).append(dur)
+        pmc = {}
+        try:
+            for name, gx, cname, val in c.execute(
+                    "select kernel_name, grid_size_x, counter_name, value from counters_collection"):
+                pmc.setdefault((_short_kernel_name(name), gx), {}).setdefault(cname, []).append(val)
+        except sqlite3.Error:
+            pass
+        cnames = sorted({n for v in pmc.values() for n in v})
+        print("| kernel | grid x | block | launches | avg us | min us | max us |"
+              + "".join(f" avg {n} |" for n in cnames))
+        print("|---|---:|---:|---:|---:|---:|---:|" + "---:|" * len(cnames))
+        for key in sorted(groups, key=lambda k: -sum(groups[k])):
+            d = groups[key]
+            vals = pmc.get((key[0], key[1]), {})
+            extra = "".join(f" {sum(vals[n]) / len(vals[n]):.1f} |" if n in vals else " |" for n in cnames)
+            print(f"| {key[0]} | {key[1]} | {key[2]} | {len(d)} | {sum(d) / len(d) / 1e3:.2f} | "
+                  f"{min(d) / 1e3:.2f} | {max(d) / 1e3:.2f} |{extra}")
+        print()
 
 
 if __name__ == "__main__":
