@@ -31,7 +31,7 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def measured_traffic(workload, kernel):
+def measured_traffic(workload, path, kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter passes
     (profiles/hbm_traffic.json: FETCH_SIZE and WRITE_SIZE scaled by a copy kernel of
     known size), or None when the kernels' source changed since the counters were taken
@@ -46,15 +46,24 @@ def measured_traffic(workload, kernel):
         return None
     if rec.get("kernel_source_sha256") != sha or rec.get("workload") != workload:
         return None
-    b = rec.get("per_launch_bytes", {}).get(kernel)
+    b = rec.get("per_launch_bytes", {}).get(path, {}).get(kernel)
     return None if b is None else int(b["read"] + b["write"])
+
+
+def step_bytes(w, direct):
+    """Algorithmic HBM bytes of one dispatch+combine over real rows.  Staged: pack reads
+    N rows and writes A, the exchange reads and writes A, the return reads and writes A,
+    the combine reads A and writes N: (2N + 6A) rows.  Direct: pack reads N and writes A
+    into the receivers' buffers, the combine reads A and writes N: 2(N + A) rows."""
+    N, A, row = w.tokens, w.assignments, w.row_bytes
+    return (2 * (N + A) if direct else 2 * N + 6 * A) * row
 
 
 def stage_bytes(w):
     """Algorithmic bytes per launch of each stage (real rows only)."""
     N, A, row = w.tokens, w.assignments, w.row_bytes
     return {
-        "plan": A * 4 + 4 * (w.num_ranks * w.num_experts + 3 * w.num_ranks * (w.num_ranks + 1)) + A * 8,
+        "plan": A * 4 + 4 * (w.num_ranks * w.num_experts + w.num_ranks * (w.num_ranks + 1)) + A * 4,
         "pack": (N + A) * row + A * 4,
         "exchange": 2 * A * row,
         "return": 2 * A * row,
@@ -71,6 +80,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode-graph", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    ap.add_argument("--paths", default="staged,direct",
+                    help="paths to time; the first one gives the headline value")
     ap.add_argument("--profile-summary", nargs="+", metavar="DB",
                     help="print per-kernel statistics of rocprofv3 database(s) and exit (no GPU)")
     args = ap.parse_args()
@@ -90,6 +101,7 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    paths = [p.strip() for p in args.paths.split(",") if p.strip()]
     w = W.workload(args.workload)
     log(f"workload {w.describe()}; generating inputs")
     x, ids, gates = W.make_inputs(w)
@@ -99,41 +111,9 @@ def main():
         xt = torch.from_numpy(x).cuda()
     idt = torch.from_numpy(ids).cuda()
     gt = torch.from_numpy(gates).cuda()
-    s = a2av.Session(w.num_ranks, w.tokens_per_rank, w.hidden, w.dtype, w.experts_per_rank, w.top_k,
-                     w.recv_capacity_rows)
-    y = torch.empty_like(xt)
-    stream = torch.cuda.current_stream()
 
-    def step():
-        s.dispatch(xt, idt)
-        s.expert(s.recv, s.recv, w.expert_mode)
-        s.combine(s.recv, gt, y)
-
-    log(f"warmup {args.warmup}")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    log(f"timing {args.steps} steps")
-    a2av.a2av_timing_begin(s.handle, args.steps)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_sum, launches = a2av.a2av_timing_end(s.handle)
-    status = int(s.status.item())
-    if status != 0:
-        raise RuntimeError(f"device status {status} during the benchmark")
-    stage_ms = {n: ms_sum[i] / max(1, launches[i]) for i, n in enumerate(a2av.STAGE_NAMES)}
-    dc_ms = sum(stage_ms.values())
-    staged = w.staged_bytes()
-    gbps = staged / (dc_ms * 1e-3) / 1e9
-    sb = stage_bytes(w)
-    dom = max((n for n in stage_ms if n != "plan"), key=lambda n: stage_ms[n])
-    dom_gbps = sb[dom] / (stage_ms[dom] * 1e-3) / 1e9
-    log("stages (ms/launch): " + ", ".join(f"{n} {v:.4f}" for n, v in stage_ms.items()))
+    measured = {p: time_path(torch, a2av, w, xt, idt, gt, p, args.steps, args.warmup) for p in paths}
+    head = measured[paths[0]]
 
     # achievable reference: a plain device copy of one stage's bytes (read + write)
     ref_elems = w.assignments * w.row_bytes // 2
@@ -152,14 +132,14 @@ def main():
 
     result = {
         "metric": "dispatch+combine µs/step and effective HBM GB/s (% of peak), 1 MI355X",
-        "value": round(gbps, 1),
+        "value": head["GBps"],
         "unit": "GB/s",
-        "us_per_step": round(dc_ms * 1e3, 2),
-        "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+        "us_per_step": head["us_per_step"],
+        "pct_hbm_peak": head["pct_hbm_peak"],
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "ms_per_step": head["ms_per_step_wall"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -168,23 +148,19 @@ def main():
         "config": {
             "workload": w.describe(),
             "virtual_ranks": w.num_ranks, "tokens_per_rank": w.tokens_per_rank, "hidden": w.hidden,
-            "experts": w.num_experts, "top_k": w.top_k, "path": "staged (pack, exchange, return, combine)",
-            "algorithmic_bytes_per_step": staged,
+            "experts": w.num_experts, "top_k": w.top_k, "path": paths[0],
+            "algorithmic_bytes_per_step": head["bytes_per_step"],
         },
-        "stage_us": {n: round(v * 1e3, 2) for n, v in stage_ms.items()},
-        "roofline": {
-            "bound": "hbm", "kernel": dom, "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic(w.name, dom),
-            "bytes_per_launch": sb[dom], "copy_reference_GBps": round(copy_gbps, 1),
-        },
+        "stage_us": head["stage_us"],
+        "roofline": dict(head["roofline"], copy_reference_GBps=round(copy_gbps, 1)),
     }
-    s.close()
-    del xt, y, s
+    for p in paths[1:]:
+        result[f"{p}_path"] = {k: v for k, v in measured[p].items() if k != "ms_per_step_wall"}
+    del xt
     torch.cuda.empty_cache()
 
     if not args.no_decode_graph:
-        result["decode_graph"] = decode_graph(np, torch, a2av, W)
+        result["decode_graph"] = {p: decode_graph(np, torch, a2av, W, p) for p in paths}
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(np, W, w, args.cpu_sample_tokens)
@@ -192,12 +168,67 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def decode_graph(np, torch, a2av, W, steps=100):
+def time_path(torch, a2av, w, xt, idt, gt, path, steps, warmup):
+    """Warm-up, then `steps` timed steps of one path with HIP events recorded between the
+    library's kernels (on the stream they run on) and the wall clock around them."""
+    direct = path == "direct"
+    s = a2av.Session(w.num_ranks, w.tokens_per_rank, w.hidden, w.dtype, w.experts_per_rank, w.top_k,
+                     w.recv_capacity_rows, path=a2av.PATH_DIRECT if direct else a2av.PATH_STAGED)
+    y = torch.empty_like(xt)
+
+    def step():
+        s.dispatch(xt, idt)
+        s.expert(s.recv, s.recv, w.expert_mode)
+        s.combine(s.recv, gt, y)
+
+    log(f"{path}: warmup {warmup}")
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"{path}: timing {steps} steps")
+    a2av.a2av_timing_begin(s.handle, steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_sum, launches = a2av.a2av_timing_end(s.handle)
+    status = int(s.status.item())
+    if status != 0:
+        raise RuntimeError(f"device status {status} during the benchmark")
+    stage_ms = {n: ms_sum[i] / launches[i] for i, n in enumerate(a2av.STAGE_NAMES) if launches[i]}
+    dc_ms = sum(stage_ms.values())
+    nbytes = step_bytes(w, direct)
+    gbps = nbytes / (dc_ms * 1e-3) / 1e9
+    sb = stage_bytes(w)
+    dom = max((n for n in stage_ms if n != "plan"), key=lambda n: stage_ms[n])
+    dom_gbps = sb[dom] / (stage_ms[dom] * 1e-3) / 1e9
+    log(f"{path}: stages (us/launch): " + ", ".join(f"{n} {v * 1e3:.1f}" for n, v in stage_ms.items()))
+    s.close()
+    del y, s
+    torch.cuda.empty_cache()
+    return {
+        "GBps": round(gbps, 1),
+        "us_per_step": round(dc_ms * 1e3, 2),
+        "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+        "ms_per_step_wall": round(wall / steps * 1e3, 4),
+        "bytes_per_step": nbytes,
+        "stage_us": {n: round(v * 1e3, 2) for n, v in stage_ms.items()},
+        "roofline": {
+            "bound": "hbm", "kernel": dom, "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": measured_traffic(w.name, path, dom), "bytes_per_launch": sb[dom],
+        },
+    }
+
+
+def decode_graph(np, torch, a2av, W, path, steps=100):
     """Decode shape: one hipGraph of router stand-in -> dispatch -> expert -> combine,
     replayed `steps` times with fresh routing taken on the device; one event pair around
     all replays, no host synchronisation between them."""
     w = W.workload("decode")
-    log(f"decode graph: {w.describe()}, {steps} replays")
+    log(f"decode graph ({path}): {w.describe()}, {steps} replays")
     x = W.make_x(w)
     n = w.tokens * w.top_k
     ids_table = torch.from_numpy(np.stack([W.make_ids(w, i).reshape(n) for i in range(steps)])).cuda()
@@ -207,7 +238,8 @@ def decode_graph(np, torch, a2av, W, steps=100):
     ids = torch.empty((w.num_ranks, w.tokens_per_rank, w.top_k), dtype=torch.int32, device="cuda")
     gates = torch.empty((w.num_ranks, w.tokens_per_rank, w.top_k), dtype=torch.float32, device="cuda")
     y = torch.empty_like(xt)
-    s = a2av.Session(w.num_ranks, w.tokens_per_rank, w.hidden, w.dtype, w.experts_per_rank, w.top_k)
+    s = a2av.Session(w.num_ranks, w.tokens_per_rank, w.hidden, w.dtype, w.experts_per_rank, w.top_k,
+                     path=a2av.PATH_DIRECT if path == "direct" else a2av.PATH_STAGED)
 
     def step():
         a2av.a2av_route_step(ids_table, gates_table, steps, n, counter, ids, gates)
@@ -238,7 +270,7 @@ def decode_graph(np, torch, a2av, W, steps=100):
     ok = int(counter.item()) == steps and int(s.status.item()) == 0
     out = {"workload": w.describe(), "replays": steps, "us_per_step_with_expert_and_router": round(us, 2),
            "host_syncs_between_replays": 0, "counter_ok": ok,
-           "algorithmic_bytes_per_step": w.staged_bytes()}
+           "algorithmic_bytes_per_step": step_bytes(w, path == "direct")}
     s.close()
     del g
     torch.cuda.empty_cache()
@@ -268,7 +300,7 @@ def cpu_baseline(np, W, w, sample_tokens):
         t3 = time.perf_counter()
         times.append((t1 - t0) + (t3 - t2))
     t = float(np.median(times))
-    gbps = ws.staged_bytes() / t / 1e9
+    gbps = step_bytes(ws, False) / t / 1e9
     try:
         with open("/proc/cpuinfo") as f:
             model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "unknown")

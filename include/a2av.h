@@ -82,6 +82,11 @@ typedef struct a2av_context* a2av_handle_t;
 #define A2AV_ST_EXPERT_RANGE  1u  /* an expert id was outside [0, E): that slot is dropped */
 #define A2AV_ST_RECV_OVERFLOW 2u  /* a rank received more rows than recv_capacity_rows */
 
+/* data paths (a2av_config_t.path) */
+#define A2AV_PATH_STAGED 0        /* pack into send segments, exchange, return, combine */
+#define A2AV_PATH_DIRECT 1        /* pack straight into the receivers' buffers; combine
+                                     gathers the expert outputs where they are */
+
 /* expert stand-ins of the harness call a2av_expert_apply */
 #define A2AV_EXPERT_IDENTITY 0    /* out = in */
 #define A2AV_EXPERT_SCALE    1    /* out = round(in * (1 + e/256)), e = the row's expert */
@@ -96,11 +101,14 @@ typedef struct {
     int64_t recv_capacity_rows; /* rows per rank's receive slice; 0 = worst case
                                    R * T * min(k, experts_per_rank).  This is an
                                    allocation size, never a transfer size. */
+    int32_t path;               /* A2AV_PATH_STAGED or A2AV_PATH_DIRECT; both give the
+                                   same receive rows, tables and combine results */
+    int32_t reserved;           /* must be 0 */
 } a2av_config_t;
 
 /* Validate cfg (host) and allocate the handle's device workspace on the current GPU:
- * the send buffer (reused as the return buffer), the position table and the
- * count/offset tables.  *out (host) receives the handle.  The workspace size is
+ * the send buffer (reused as the return buffer; staged path only), the position table
+ * and the count/offset tables.  *out (host) receives the handle.  The workspace size is
  * a2av_workspace_bytes(cfg).  Errors: A2AV_ERR_INVALID, A2AV_ERR_NOMEM, A2AV_ERR_HIP. */
 int a2av_create(const a2av_config_t* cfg, a2av_handle_t* out);
 
@@ -114,11 +122,13 @@ int64_t a2av_workspace_bytes(const a2av_config_t* cfg);
 /* Dispatch (the token sort and the all-to-allv, abhik.ai page, Figure 13):
  *   1. histogram: rows per (rank, expert), from topk_ids, on the GPU;
  *   2. scans: per-rank expert and destination offsets; the received counts and
- *      offsets of every rank, formed from every sender's split table on the GPU;
+ *      offsets of every rank, formed from every sender's offsets on the GPU;
  *   3. pack: every (token, slot) row of x copied to its place in the sender's send
  *      segments, stable by (expert, token, slot);
  *   4. exchange: every segment copied into the receiving rank's slice of recv at the
  *      offset the device tables give.
+ * The direct path fuses 3 and 4: each row goes from x straight to its receive place
+ * (the pages' zero-copy transfer, user buffer to peer user buffer).
  * x (device) [R][T][H] dtype; topk_ids (device) [R][T][k].  recv (device, caller
  * owned) [R][cap][H]: only the first min(recv_offsets[d][R], cap) rows of slice d are
  * written.  split, recv_counts, recv_offsets (device, optional: NULL = not wanted)
@@ -130,7 +140,8 @@ int a2av_dispatch(a2av_handle_t h, const void* x, const int32_t* topk_ids, void*
 
 /* Combine (the return all-to-all and the merge, qiguanping.github.io page, section 7,
  * figure 13): every expert-output row goes back to the place its input row had in the
- * sender's send segments, then every token's output is
+ * sender's send segments (the direct path reads it where it is instead), then every
+ * token's output is
  *   y[s][t] = round_to_dtype( sum_{j<k} gates[s][t][j] * out_j ),
  * summed in float32 with one fused multiply-add per slot in slot order, rounded once
  * (nearest, ties to even).  expert_out (device) [R][cap][H] in the receive layout of
@@ -184,7 +195,8 @@ int a2av_route_step(const int32_t* ids_table, const float* gates_table, int32_t 
  * the recorded events, writes per-stage sums of milliseconds into ms_sum (host)
  * [A2AV_STAGES] and the number of timed launches per stage into launches (host)
  * [A2AV_STAGES], and releases the events.  Stages: 0 plan (histogram + scans), 1 pack,
- * 2 exchange, 3 return exchange, 4 combine. */
+ * 2 exchange, 3 return exchange, 4 combine (the direct path has no 2 and 3).  Events
+ * recorded between kernels add a little time to each step while timing is on. */
 #define A2AV_STAGES 5
 int a2av_timing_begin(a2av_handle_t h, int32_t max_calls);
 int a2av_timing_end(a2av_handle_t h, double* ms_sum, int32_t* launches);

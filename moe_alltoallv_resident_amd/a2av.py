@@ -20,6 +20,8 @@ ST_EXPERT_RANGE = 1
 ST_RECV_OVERFLOW = 2
 EXPERT_IDENTITY = 0
 EXPERT_SCALE = 1
+PATH_STAGED = 0
+PATH_DIRECT = 1
 STAGES = 5
 STAGE_NAMES = ("plan", "pack", "exchange", "return", "combine")
 
@@ -35,7 +37,7 @@ class Config(ctypes.Structure):
     _fields_ = [("num_ranks", ctypes.c_int32), ("tokens_per_rank", ctypes.c_int32),
                 ("hidden", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("experts_per_rank", ctypes.c_int32), ("top_k", ctypes.c_int32),
-                ("recv_capacity_rows", ctypes.c_int64)]
+                ("recv_capacity_rows", ctypes.c_int64), ("path", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class A2AVError(RuntimeError):
@@ -105,8 +107,9 @@ def _check(fn, rc):
         raise A2AVError(fn, rc)
 
 
-def make_config(num_ranks, tokens_per_rank, hidden, dtype, experts_per_rank, top_k, recv_capacity_rows=0) -> Config:
-    return Config(num_ranks, tokens_per_rank, hidden, dtype, experts_per_rank, top_k, recv_capacity_rows)
+def make_config(num_ranks, tokens_per_rank, hidden, dtype, experts_per_rank, top_k, recv_capacity_rows=0,
+                path=PATH_STAGED) -> Config:
+    return Config(num_ranks, tokens_per_rank, hidden, dtype, experts_per_rank, top_k, recv_capacity_rows, path, 0)
 
 
 def a2av_workspace_bytes(cfg: Config) -> int:
@@ -178,9 +181,10 @@ class Session:
     """
 
     def __init__(self, num_ranks, tokens_per_rank, hidden, dtype, experts_per_rank, top_k,
-                 recv_capacity_rows=0, device="cuda"):
+                 recv_capacity_rows=0, path=PATH_STAGED, device="cuda"):
         self.cfg = make_config(num_ranks, tokens_per_rank, hidden, dtype, experts_per_rank, top_k,
-                               recv_capacity_rows)
+                               recv_capacity_rows, path)
+        self.path = path
         self.R, self.T, self.H, self.k = num_ranks, tokens_per_rank, hidden, top_k
         self.E = num_ranks * experts_per_rank
         self.cap = recv_capacity_rows or num_ranks * tokens_per_rank * min(top_k, experts_per_rank)

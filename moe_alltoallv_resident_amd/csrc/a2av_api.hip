@@ -10,20 +10,24 @@
 using a2av::Shape;
 using a2av::Tables;
 
+// One timed kernel launch: stage id and the events recorded around it.
+struct TimedLaunch {
+    int stage;
+    hipEvent_t a, b;
+};
+
 struct a2av_context {
     a2av_config_t cfg;
     Shape sh;
     int device;
-    void* send_buf;       // [R][T*k][row]: send segments, then the return buffer
+    bool direct;          // A2AV_PATH_DIRECT: no send buffer, rows go straight to receivers
+    void* send_buf;       // [R][T*k][row]: send segments, then the return buffer (staged)
     void* meta;           // tables
     size_t meta_bytes;
     Tables tb;
     bool routed;          // latest planning came from a2av_dispatch (combine allowed)
-    // stage timing
-    std::vector<hipEvent_t> ev;      // per timed call: dispatch 4, combine 3 events
-    int32_t timing_max;
-    int32_t timed_dispatch;
-    int32_t timed_combine;
+    std::vector<TimedLaunch> timed;  // stage timing slots
+    size_t timed_used;
 };
 
 namespace {
@@ -54,6 +58,8 @@ bool make_shape(const a2av_config_t* c, Shape* sh) {
     int64_t cap = c->recv_capacity_rows;
     if (cap == 0) cap = (int64_t)c->num_ranks * c->tokens_per_rank * std::min<int64_t>(c->top_k, c->experts_per_rank);
     if (cap > INT32_MAX) return false;
+    if (c->path != A2AV_PATH_STAGED && c->path != A2AV_PATH_DIRECT) return false;
+    if (c->reserved != 0) return false;
     sh->R = c->num_ranks;
     sh->T = c->tokens_per_rank;
     sh->k = c->top_k;
@@ -69,7 +75,7 @@ bool make_shape(const a2av_config_t* c, Shape* sh) {
 }
 
 struct MetaLayout {
-    size_t pos, cnt, send_off, recv_counts, recv_off, ticket, total;
+    size_t pos, cnt, send_off, recv_counts, recv_off, total;
 };
 
 MetaLayout meta_layout(const Shape& sh) {
@@ -80,12 +86,14 @@ MetaLayout meta_layout(const Shape& sh) {
     m.send_off = o;    o += align_up(sizeof(int32_t) * (size_t)sh.R * (sh.R + 1));
     m.recv_counts = o; o += align_up(sizeof(int32_t) * (size_t)sh.R * sh.R);
     m.recv_off = o;    o += align_up(sizeof(int32_t) * (size_t)sh.R * (sh.R + 1));
-    m.ticket = o;      o += kAlign;
     m.total = o;
     return m;
 }
 
-size_t send_bytes(const Shape& sh) { return (size_t)sh.R * (size_t)sh.TK * (size_t)sh.row_bytes; }
+size_t send_bytes(const a2av_config_t* c, const Shape& sh) {
+    if (c->path == A2AV_PATH_DIRECT) return 0;
+    return (size_t)sh.R * (size_t)sh.TK * (size_t)sh.row_bytes;
+}
 
 bool on_device(const a2av_context* h) {
     int dev = -1;
@@ -97,15 +105,29 @@ int min_vec(const Shape& sh) { return sh.dtype == A2AV_F32 ? 4 : 2; }
 // Row arrays are empty when there are no tokens; their pointers may then be null.
 bool has_tokens(const Shape& sh) { return sh.T > 0; }
 
-// Timing: event slots of the next dispatch / combine call, or null when not timing.
-hipEvent_t* dispatch_events(a2av_context* h) {
-    if (h->timed_dispatch >= h->timing_max) return nullptr;
-    return &h->ev[(size_t)h->timed_dispatch++ * 7];
+// Launch one kernel, with timing events around it while timing slots remain.
+template <typename F>
+int launch_timed(a2av_context* h, int stage, hipStream_t st, F&& launch) {
+    TimedLaunch* t = h->timed_used < h->timed.size() ? &h->timed[h->timed_used++] : nullptr;
+    if (t) {
+        t->stage = stage;
+        if (hipEventRecord(t->a, st) != hipSuccess) return A2AV_ERR_HIP;
+    }
+    if (launch() != hipSuccess) return A2AV_ERR_HIP;
+    if (t && hipEventRecord(t->b, st) != hipSuccess) return A2AV_ERR_HIP;
+    return A2AV_OK;
 }
-hipEvent_t* combine_events(a2av_context* h) {
-    if (h->timed_combine >= h->timing_max) return nullptr;
-    return &h->ev[(size_t)h->timed_combine++ * 7 + 4];
+
+void drop_timing(a2av_context* h) {
+    for (TimedLaunch& t : h->timed) {
+        (void)hipEventDestroy(t.a);
+        (void)hipEventDestroy(t.b);
+    }
+    h->timed.clear();
+    h->timed_used = 0;
 }
+
+enum { kStagePlan = 0, kStagePack = 1, kStageExchange = 2, kStageReturn = 3, kStageCombine = 4 };
 
 }  // namespace
 
@@ -124,7 +146,7 @@ const char* a2av_error_string(int code) {
 int64_t a2av_workspace_bytes(const a2av_config_t* cfg) {
     Shape sh;
     if (!make_shape(cfg, &sh)) return -1;
-    return (int64_t)(align_up(send_bytes(sh)) + meta_layout(sh).total);
+    return (int64_t)(align_up(send_bytes(cfg, sh)) + meta_layout(sh).total);
 }
 
 int a2av_create(const a2av_config_t* cfg, a2av_handle_t* out) {
@@ -136,9 +158,10 @@ int a2av_create(const a2av_config_t* cfg, a2av_handle_t* out) {
     if (!h) return A2AV_ERR_NOMEM;
     h->cfg = *cfg;
     h->sh = sh;
+    h->direct = cfg->path == A2AV_PATH_DIRECT;
     if (hipGetDevice(&h->device) != hipSuccess) { delete h; return A2AV_ERR_HIP; }
     const MetaLayout m = meta_layout(sh);
-    const size_t sb = std::max<size_t>(send_bytes(sh), kAlign);
+    const size_t sb = std::max<size_t>(send_bytes(cfg, sh), kAlign);
     if (hipMalloc(&h->send_buf, sb) != hipSuccess) { (void)hipGetLastError(); delete h; return A2AV_ERR_NOMEM; }
     if (hipMalloc(&h->meta, m.total) != hipSuccess) {
         (void)hipGetLastError();
@@ -153,9 +176,7 @@ int a2av_create(const a2av_config_t* cfg, a2av_handle_t* out) {
     h->tb.send_off = reinterpret_cast<int32_t*>(b + m.send_off);
     h->tb.recv_counts = reinterpret_cast<int32_t*>(b + m.recv_counts);
     h->tb.recv_off = reinterpret_cast<int32_t*>(b + m.recv_off);
-    h->tb.ticket = reinterpret_cast<uint32_t*>(b + m.ticket);
-    // tables start at zero (a combine before any dispatch moves nothing) and so does
-    // the planning grid's arrival ticket
+    // tables start at zero
     if (hipMemset(h->meta, 0, m.total) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
         (void)hipFree(h->meta);
         (void)hipFree(h->send_buf);
@@ -163,8 +184,7 @@ int a2av_create(const a2av_config_t* cfg, a2av_handle_t* out) {
         return A2AV_ERR_HIP;
     }
     h->routed = false;
-    h->timing_max = 0;
-    h->timed_dispatch = h->timed_combine = 0;
+    h->timed_used = 0;
     *out = h;
     return A2AV_OK;
 }
@@ -172,8 +192,7 @@ int a2av_create(const a2av_config_t* cfg, a2av_handle_t* out) {
 int a2av_destroy(a2av_handle_t h) {
     if (!h) return A2AV_OK;
     int rc = A2AV_OK;
-    for (hipEvent_t e : h->ev)
-        if (hipEventDestroy(e) != hipSuccess) rc = A2AV_ERR_HIP;
+    drop_timing(h);
     if (hipFree(h->meta) != hipSuccess) rc = A2AV_ERR_HIP;
     if (hipFree(h->send_buf) != hipSuccess) rc = A2AV_ERR_HIP;
     delete h;
@@ -189,15 +208,20 @@ int a2av_dispatch(a2av_handle_t h, const void* x, const int32_t* topk_ids, void*
     const int vec = a2av::pick_vec_bytes(sh.row_bytes, ptrs, 3);
     if (vec < min_vec(sh)) return A2AV_ERR_INVALID;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    hipEvent_t* ev = dispatch_events(h);
-    a2av::Outputs out{split, recv_counts, recv_offsets};
-    if (ev && hipEventRecord(ev[0], st) != hipSuccess) return A2AV_ERR_HIP;
-    if (a2av::launch_plan(sh, h->tb, topk_ids, out, status, st) != hipSuccess) return A2AV_ERR_HIP;
-    if (ev && hipEventRecord(ev[1], st) != hipSuccess) return A2AV_ERR_HIP;
-    if (a2av::launch_pack(sh, h->tb, x, h->send_buf, vec, st) != hipSuccess) return A2AV_ERR_HIP;
-    if (ev && hipEventRecord(ev[2], st) != hipSuccess) return A2AV_ERR_HIP;
-    if (a2av::launch_exchange(sh, h->tb, h->send_buf, recv, false, vec, st) != hipSuccess) return A2AV_ERR_HIP;
-    if (ev && hipEventRecord(ev[3], st) != hipSuccess) return A2AV_ERR_HIP;
+    const a2av::Outputs out{split, recv_counts, recv_offsets};
+    const a2av::Tables& tb = h->tb;
+    int rc = launch_timed(h, kStagePlan, st, [&] { return a2av::launch_plan(sh, tb, topk_ids, out, status, st); });
+    if (rc != A2AV_OK) return rc;
+    void* dst = h->direct ? recv : h->send_buf;
+    rc = launch_timed(h, kStagePack, st,
+                      [&] { return a2av::launch_pack(sh, tb, out, status, x, dst, h->direct, vec, st); });
+    if (rc != A2AV_OK) return rc;
+    if (!h->direct && sh.TK > 0) {
+        rc = launch_timed(h, kStageExchange, st, [&] {
+            return a2av::launch_exchange(sh, tb, out, status, h->send_buf, recv, false, false, vec, st);
+        });
+        if (rc != A2AV_OK) return rc;
+    }
     h->routed = true;
     return A2AV_OK;
 }
@@ -210,14 +234,19 @@ int a2av_combine(a2av_handle_t h, const void* expert_out, const float* gates, vo
     const void* ptrs[] = {expert_out, y, h->send_buf};
     const int vec = a2av::pick_vec_bytes(sh.row_bytes, ptrs, 3);
     if (vec < min_vec(sh) || ((uintptr_t)gates % 4) != 0) return A2AV_ERR_INVALID;
+    if (!has_tokens(sh)) return A2AV_OK;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    hipEvent_t* ev = combine_events(h);
-    if (ev && hipEventRecord(ev[0], st) != hipSuccess) return A2AV_ERR_HIP;
-    if (a2av::launch_exchange(sh, h->tb, expert_out, h->send_buf, true, vec, st) != hipSuccess) return A2AV_ERR_HIP;
-    if (ev && hipEventRecord(ev[1], st) != hipSuccess) return A2AV_ERR_HIP;
-    if (a2av::launch_combine(sh, h->tb, h->send_buf, gates, y, vec, st) != hipSuccess) return A2AV_ERR_HIP;
-    if (ev && hipEventRecord(ev[2], st) != hipSuccess) return A2AV_ERR_HIP;
-    return A2AV_OK;
+    const a2av::Tables& tb = h->tb;
+    const a2av::Outputs none{nullptr, nullptr, nullptr};
+    if (!h->direct) {
+        int rc = launch_timed(h, kStageReturn, st, [&] {
+            return a2av::launch_exchange(sh, tb, none, status, expert_out, h->send_buf, true, false, vec, st);
+        });
+        if (rc != A2AV_OK) return rc;
+    }
+    const void* rows = h->direct ? expert_out : h->send_buf;
+    return launch_timed(h, kStageCombine, st,
+                        [&] { return a2av::launch_combine(sh, tb, rows, gates, y, h->direct, vec, st); });
 }
 
 int a2av_alltoallv(a2av_handle_t h, const void* send, const int32_t* send_counts, void* recv, int32_t* recv_counts,
@@ -230,9 +259,10 @@ int a2av_alltoallv(a2av_handle_t h, const void* send, const int32_t* send_counts
     if (vec < min_vec(sh)) return A2AV_ERR_INVALID;
     hipStream_t st = static_cast<hipStream_t>(stream);
     h->routed = false;
-    a2av::Outputs out{nullptr, recv_counts, recv_offsets};
-    if (a2av::launch_plan_from_counts(sh, h->tb, send_counts, out, status, st) != hipSuccess) return A2AV_ERR_HIP;
-    if (a2av::launch_exchange(sh, h->tb, send, recv, false, vec, st) != hipSuccess) return A2AV_ERR_HIP;
+    const a2av::Outputs out{nullptr, recv_counts, recv_offsets};
+    if (a2av::launch_plan_from_counts(sh, h->tb, send_counts, status, st) != hipSuccess) return A2AV_ERR_HIP;
+    if (a2av::launch_exchange(sh, h->tb, out, status, send, recv, false, true, vec, st) != hipSuccess)
+        return A2AV_ERR_HIP;
     return A2AV_OK;
 }
 
@@ -273,15 +303,16 @@ int a2av_route_step(const int32_t* ids_table, const float* gates_table, int32_t 
 
 int a2av_timing_begin(a2av_handle_t h, int32_t max_calls) {
     if (!h || max_calls < 1) return A2AV_ERR_INVALID;
-    for (hipEvent_t e : h->ev) (void)hipEventDestroy(e);
-    h->ev.assign((size_t)max_calls * 7, nullptr);
-    for (auto& e : h->ev)
-        if (hipEventCreate(&e) != hipSuccess) {
-            h->timing_max = 0;
+    drop_timing(h);
+    h->timed.resize((size_t)max_calls * A2AV_STAGES);
+    for (TimedLaunch& t : h->timed) {
+        t.a = t.b = nullptr;
+        if (hipEventCreate(&t.a) != hipSuccess || hipEventCreate(&t.b) != hipSuccess) {
+            drop_timing(h);
             return A2AV_ERR_HIP;
         }
-    h->timing_max = max_calls;
-    h->timed_dispatch = h->timed_combine = 0;
+    }
+    h->timed_used = 0;
     return A2AV_OK;
 }
 
@@ -289,30 +320,17 @@ int a2av_timing_end(a2av_handle_t h, double* ms_sum, int32_t* launches) {
     if (!h || !ms_sum || !launches) return A2AV_ERR_INVALID;
     for (int i = 0; i < A2AV_STAGES; ++i) { ms_sum[i] = 0.0; launches[i] = 0; }
     int rc = A2AV_OK;
-    auto add = [&](hipEvent_t a, hipEvent_t b, int stage) {
+    for (size_t i = 0; i < h->timed_used; ++i) {
+        const TimedLaunch& t = h->timed[i];
         float ms = 0.0f;
-        if (hipEventSynchronize(b) != hipSuccess || hipEventElapsedTime(&ms, a, b) != hipSuccess) {
+        if (hipEventSynchronize(t.b) != hipSuccess || hipEventElapsedTime(&ms, t.a, t.b) != hipSuccess) {
             rc = A2AV_ERR_HIP;
-            return;
+            continue;
         }
-        ms_sum[stage] += ms;
-        launches[stage] += 1;
-    };
-    for (int32_t c = 0; c < h->timed_dispatch; ++c) {
-        hipEvent_t* e = &h->ev[(size_t)c * 7];
-        add(e[0], e[1], 0);
-        add(e[1], e[2], 1);
-        add(e[2], e[3], 2);
+        ms_sum[t.stage] += ms;
+        launches[t.stage] += 1;
     }
-    for (int32_t c = 0; c < h->timed_combine; ++c) {
-        hipEvent_t* e = &h->ev[(size_t)c * 7 + 4];
-        add(e[0], e[1], 3);
-        add(e[1], e[2], 4);
-    }
-    for (hipEvent_t e : h->ev) (void)hipEventDestroy(e);
-    h->ev.clear();
-    h->timing_max = 0;
-    h->timed_dispatch = h->timed_combine = 0;
+    drop_timing(h);
     return rc;
 }
 

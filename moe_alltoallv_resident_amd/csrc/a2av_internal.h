@@ -27,8 +27,7 @@ struct Tables {
     int32_t* cnt;          // [R][E]    rows per (source rank, expert)
     int32_t* send_off;     // [R][R+1]  segment starts in each send buffer
     int32_t* recv_counts;  // [R][R]    [dst][src]
-    int32_t* recv_off;     // [R][R+1]  [dst][src] exclusive prefix over src
-    uint32_t* ticket;      // arrival counter of the planning grid (reset by its last block)
+    int32_t* recv_off;     // [R][R+1]  [dst][src] exclusive prefix over src, [dst][R] total
 };
 
 // Optional copies of the tables for the caller (any may be null).
@@ -42,16 +41,24 @@ struct Outputs {
 // the row size and the alignment of every base address involved.
 int pick_vec_bytes(int64_t row_bytes, const void* const* ptrs, int nptrs);
 
+// Wavefronts per planning block for E experts (LDS holds (waves + 1) * E counters).
+int plan_waves(int32_t E);
+
 hipError_t launch_plan(const Shape& sh, const Tables& tb, const int32_t* ids, const Outputs& out,
                        uint32_t* status, hipStream_t st);
 hipError_t launch_plan_from_counts(const Shape& sh, const Tables& tb, const int32_t* send_counts,
-                                   const Outputs& out, uint32_t* status, hipStream_t st);
-hipError_t launch_pack(const Shape& sh, const Tables& tb, const void* x, void* send, int vec,
-                       hipStream_t st);
-hipError_t launch_exchange(const Shape& sh, const Tables& tb, const void* src, void* dst, bool reverse,
-                           int vec, hipStream_t st);
-hipError_t launch_combine(const Shape& sh, const Tables& tb, const void* ret, const float* gates, void* y,
-                          int vec, hipStream_t st);
+                                   uint32_t* status, hipStream_t st);
+// pack: staged (dst = send buffer) or direct (dst = receive buffer); also builds the
+// receive tables (and the caller's copies in `out`).
+hipError_t launch_pack(const Shape& sh, const Tables& tb, const Outputs& out, uint32_t* status, const void* x,
+                       void* dst, bool direct, int vec, hipStream_t st);
+// exchange: forward (send -> recv) or reverse (recv layout -> send places); `first`
+// when it directly follows planning (builds the receive tables itself).
+hipError_t launch_exchange(const Shape& sh, const Tables& tb, const Outputs& out, uint32_t* status,
+                           const void* src, void* dst, bool reverse, bool first, int vec, hipStream_t st);
+// combine: rows = return buffer (staged) or expert outputs in the receive layout (direct).
+hipError_t launch_combine(const Shape& sh, const Tables& tb, const void* rows, const float* gates, void* y,
+                          bool direct, int vec, hipStream_t st);
 hipError_t launch_expert(const Shape& sh, const Tables& tb, const void* in, void* out, int mode, int vec,
                          hipStream_t st);
 hipError_t launch_route_step(const int32_t* ids_table, const float* gates_table, int32_t steps, int64_t n,

@@ -3,16 +3,22 @@
 // The path follows the pages' mixture-of-experts layer (abhik.ai "Collective
 // Communication for 100k+ GPUs", section "Inference: small messages, unknown sizes",
 // Figure 13; qiguanping.github.io "NCCLX", section 7, figures 13-18):
-//   plan      histogram of (rank, expert) and the scans that turn it into send and
-//             receive offsets, all on the device (the GPU-resident metadata);
-//   pack      token rows copied into expert-sorted send segments;
-//   exchange  segments copied into the receiving ranks' buffers at device-computed
-//             offsets (the all-to-allv), and the same kernel reversed for the return;
-//   combine   gate-weighted sum of each token's k returned rows, float32 accumulate.
-// Everything but the planning kernel is a row copy or a row gather, bound by HBM
-// bandwidth: rows move as 16-byte vectors, one 64-lane wavefront per row, with all of
-// a row's loads issued before its stores.  Nothing here is a dense contraction, so no
-// matrix-core instruction is used.
+//   plan      per rank: histogram of (rank, expert), the scans that turn it into send
+//             offsets, and every assignment's stable place in the expert-sorted order
+//             (the GPU-resident metadata);
+//   tables    every receiver's counts and offsets, formed from all senders' send
+//             offsets by the first kernel that runs after planning (the metadata
+//             exchange between ranks, with no host involved);
+//   pack      token rows copied into expert-sorted send segments (staged path) or
+//             straight into the receiving ranks' buffers (direct path);
+//   exchange  staged path: segments copied into the receiving ranks' buffers at
+//             device-computed offsets (the all-to-allv), and reversed for the return;
+//   combine   gate-weighted sum of each token's k expert rows, float32 accumulate,
+//             reading the return buffer (staged) or the expert outputs in place (direct).
+// Everything but planning is a row copy or gather bound by HBM bandwidth: rows move as
+// 16-byte vectors, one 64-lane wavefront per row, with all of a row's loads issued
+// before its stores, non-temporal for buffers too large to stay in cache.  Nothing here
+// is a dense contraction, so no matrix-core instruction is used.
 #include "a2av_internal.h"
 
 #include <algorithm>
@@ -50,11 +56,21 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
     return v;
 }
 
-__device__ __forceinline__ int32_t load_agent(const int32_t* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+    for (int d = kWave / 2; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
+    return v;
 }
-__device__ __forceinline__ void store_agent(int32_t* p, int32_t v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+template <bool NT, typename V>
+__device__ __forceinline__ V ld(const V* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+template <bool NT, typename V>
+__device__ __forceinline__ void st(V* p, const V& v) {
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
 }
 
 // Exclusive prefix sum of a[0..n) in LDS, in place, by the whole block; returns the
@@ -81,61 +97,65 @@ __device__ int block_exclusive_scan(int* a, int n, int* wsum) {
     return total;
 }
 
-// Receive side of the metadata exchange, run by the last block of a planning grid once
-// every sender has published its column recv_counts[.][s]: for every destination d,
-// recv_off[d][s] = sum over s' < s of recv_counts[d][s'] (one wavefront per d).
-__device__ void finish_recv_tables(const Shape& sh, const Tables& tb, const Outputs& out, uint32_t* status) {
-    const int R = sh.R, lane = lane_id(), w = threadIdx.x / kWave, nw = blockDim.x / kWave;
-    for (int d = w; d < R; d += nw) {
-        int carry = 0;
-        for (int s0 = 0; s0 < R; s0 += kWave) {
-            const int s = s0 + lane;
-            const int c = s < R ? load_agent(tb.recv_counts + (int64_t)d * R + s) : 0;
-            const int incl = wave_inclusive_scan(c);
-            if (s < R) {
-                const int off = carry + incl - c;
-                tb.recv_off[(int64_t)d * (R + 1) + s] = off;
-                if (out.recv_off) out.recv_off[(int64_t)d * (R + 1) + s] = off;
-                if (out.recv_counts) out.recv_counts[(int64_t)d * R + s] = c;
-            }
-            carry += __shfl(incl, kWave - 1, kWave);
+// ---- the metadata exchange ------------------------------------------------------------
+// Rows rank d gets from sender s: the length of s's segment for d.
+__device__ __forceinline__ int seg_len(const int32_t* send_off, int R, int s, int d) {
+    const int32_t* so = send_off + (int64_t)s * (R + 1);
+    return so[d + 1] - so[d];
+}
+
+// recv_off[d][s] computed from the senders' send offsets (whole wavefront, uniform
+// result): the rows d receives from the senders before s.
+__device__ __forceinline__ int64_t recv_base(const int32_t* send_off, int R, int d, int s, int lane) {
+    int acc = 0;
+    for (int c0 = 0; c0 < s; c0 += kWave) {
+        const int sp = c0 + lane;
+        if (sp < s) acc += seg_len(send_off, R, sp, d);
+    }
+    return wave_sum(acc);
+}
+
+// Receiver d's table row (one wavefront): recv_counts[d][s], recv_off[d][s] (exclusive
+// prefix over s) and the total; flags a receiver whose rows exceed its capacity.
+__device__ void write_recv_tables(const Shape& sh, const Tables& tb, const Outputs& out, uint32_t* status, int d,
+                                  int lane) {
+    const int R = sh.R;
+    int carry = 0;
+    for (int s0 = 0; s0 < R; s0 += kWave) {
+        const int s = s0 + lane;
+        const int c = s < R ? seg_len(tb.send_off, R, s, d) : 0;
+        const int incl = wave_inclusive_scan(c);
+        if (s < R) {
+            const int off = carry + incl - c;
+            tb.recv_counts[(int64_t)d * R + s] = c;
+            tb.recv_off[(int64_t)d * (R + 1) + s] = off;
+            if (out.recv_counts) out.recv_counts[(int64_t)d * R + s] = c;
+            if (out.recv_off) out.recv_off[(int64_t)d * (R + 1) + s] = off;
         }
-        if (lane == 0) {
-            tb.recv_off[(int64_t)d * (R + 1) + R] = carry;
-            if (out.recv_off) out.recv_off[(int64_t)d * (R + 1) + R] = carry;
-            if ((int64_t)carry > sh.cap) atomicOr(status, 2u);
-        }
+        carry += __shfl(incl, kWave - 1, kWave);
+    }
+    if (lane == 0) {
+        tb.recv_off[(int64_t)d * (R + 1) + R] = carry;
+        if (out.recv_off) out.recv_off[(int64_t)d * (R + 1) + R] = carry;
+        if ((int64_t)carry > sh.cap) atomicOr(status, 2u);
     }
 }
 
-// Arrival ticket: returns true in exactly one block, the last to arrive, after all
-// blocks' earlier global writes are visible to it.  The last block resets the ticket
-// so the next launch (or graph replay) starts from zero.
-__device__ bool last_block_arrives(uint32_t* ticket, int* flag) {
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t prev = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        *flag = (prev == gridDim.x - 1) ? 1 : 0;
-    }
-    __syncthreads();
-    if (!*flag) return false;
-    __threadfence();
-    return true;
-}
+// Blocks that build the receive tables come first in the grid of the kernel that
+// follows planning: one wavefront per receiver.
+__host__ __device__ __forceinline__ int64_t table_blocks(int R) { return (R + kRowsPerBlock - 1) / kRowsPerBlock; }
 
 // ------------------------------------------------------------------------------------
-// plan: one block per rank (histogram, scans, stable positions), then the last block
-// forms every rank's receive offsets.
+// plan: one block per rank (histogram, scans, stable positions, send offsets).
 //
 // Positions are a stable counting sort by (expert, token, slot).  Each wavefront owns a
-// contiguous run of the rank's assignments and walks it 64 at a time.  Lanes holding
-// the same expert find each other with one ballot per bit of the expert id (the AND of
-// the matching ballots is the set of lanes with an equal id); a lane's rank among them
-// is the popcount of that set below it.  The lowest such lane adds the group size to
-// the wavefront's private LDS counter for that expert, so no atomics are needed and the
-// result does not depend on timing.  Counters of all wavefronts are then scanned in
-// (expert, wavefront) order into final bases.
+// contiguous run of the rank's assignments and takes it in batches of S x 64, loading a
+// whole batch before using it.  Lanes holding the same expert find each other with one
+// ballot per bit of the expert id (the AND of the matching ballots is the set of lanes
+// with an equal id); a lane's rank among them is the popcount of that set below it.  The
+// lowest such lane adds the group size to the wavefront's private LDS counter for that
+// expert, so no atomics are needed and the result does not depend on timing.  Counters
+// of all wavefronts are then scanned in (expert, wavefront) order into final bases.
 // ------------------------------------------------------------------------------------
 struct PlanArgs {
     Shape sh;
@@ -145,10 +165,10 @@ struct PlanArgs {
     uint32_t* status;
 };
 
+template <int S>
 __global__ void __launch_bounds__(1024) plan_kernel(PlanArgs a) {
     extern __shared__ int lds[];
     __shared__ int wsum[17];
-    __shared__ int flag;
     const Shape& sh = a.sh;
     const int E = sh.E, R = sh.R;
     const int tid = threadIdx.x, nt = blockDim.x, lane = lane_id(), w = tid / kWave, nw = nt / kWave;
@@ -164,27 +184,40 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanArgs a) {
     int32_t* pos = a.tb.pos + (int64_t)s * TK;
     const int64_t chunk = ((TK + nw - 1) / nw + kWave - 1) / kWave * kWave;
     const int64_t a0 = min(TK, (int64_t)w * chunk), a1 = min(TK, a0 + chunk);
+    const int64_t batch = (int64_t)S * kWave;
+    const bool one_batch = a1 - a0 <= batch;
     int* mine = cw + w * E;
     bool bad = false;
+    int ev[S], rk[S];
 
     // pass 1: rank of every assignment among equal experts inside its wavefront's run
-    for (int64_t base = a0; base < a1; base += kWave) {
-        const int64_t i = base + lane;
-        const bool valid = i < a1;
-        const int e = valid ? ids[i] : 0;
-        const bool in = valid && e >= 0 && e < E;
-        bad |= valid && !in;
-        uint64_t match = __ballot(in);
-        for (int b = 0; b < sh.nbits; ++b) {
-            const bool bit = (e >> b) & 1;
-            const uint64_t m = __ballot(in && bit);
-            match &= bit ? m : ~m;
+    for (int64_t b0 = a0; b0 < a1; b0 += batch) {
+#pragma unroll
+        for (int u = 0; u < S; ++u) {
+            const int64_t i = b0 + u * kWave + lane;
+            ev[u] = i < a1 ? ids[i] : 0;
         }
-        if (in) {
-            const int r = __popcll(match & lanes_below(lane));
-            const int c = mine[e];
-            pos[i] = c + r;
-            if (r == 0) mine[e] = c + __popcll(match);
+#pragma unroll
+        for (int u = 0; u < S; ++u) {
+            const int64_t i = b0 + u * kWave + lane;
+            const bool valid = i < a1;
+            const int e = ev[u];
+            const bool in = valid && e >= 0 && e < E;
+            bad |= valid && !in;
+            uint64_t match = __ballot(in);
+            for (int b = 0; b < sh.nbits; ++b) {
+                const bool bit = (e >> b) & 1;
+                const uint64_t m = __ballot(in && bit);
+                match &= bit ? m : ~m;
+            }
+            rk[u] = -1;
+            if (in) {
+                const int r = __popcll(match & lanes_below(lane));
+                const int c = mine[e];
+                rk[u] = c + r;
+                if (r == 0) mine[e] = c + __popcll(match);
+            }
+            if (!one_batch && valid) pos[i] = rk[u];
         }
     }
     if (__ballot(bad) != 0 && lane == 0) atomicOr(a.status, 1u);
@@ -203,36 +236,29 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanArgs a) {
 
     // send segments: destination d holds experts d*epr .. d*epr+epr-1, which are
     // consecutive in the sorted order
-    for (int d = tid; d <= R; d += nt) {
-        const int lo = d < R ? tot[d * sh.epr] : total;
-        a.tb.send_off[(int64_t)s * (R + 1) + d] = lo;
-        if (d < R) {
-            const int hi = d + 1 < R ? tot[(d + 1) * sh.epr] : total;
-            store_agent(a.tb.recv_counts + (int64_t)d * R + s, hi - lo);   // column s of [dst][src]
-        }
-    }
+    for (int d = tid; d <= R; d += nt) a.tb.send_off[(int64_t)s * (R + 1) + d] = d < R ? tot[d * sh.epr] : total;
     for (int i = tid; i < nw * E; i += nt) cw[i] += tot[i % E];
     __syncthreads();
 
     // pass 2: final positions
-    for (int64_t base = a0; base < a1; base += kWave) {
-        const int64_t i = base + lane;
-        if (i < a1) {
+    if (one_batch) {
+#pragma unroll
+        for (int u = 0; u < S; ++u) {
+            const int64_t i = a0 + u * kWave + lane;
+            if (i < a1) pos[i] = rk[u] >= 0 ? mine[ev[u]] + rk[u] : -1;
+        }
+    } else {
+        for (int64_t i = a0 + lane; i < a1; i += kWave) {
             const int e = ids[i];
             pos[i] = (e >= 0 && e < E) ? mine[e] + pos[i] : -1;
         }
     }
-
-    if (!last_block_arrives(a.tb.ticket, &flag)) return;
-    finish_recv_tables(sh, a.tb, a.out, a.status);
-    if (tid == 0) __hip_atomic_store(a.tb.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The bare collective's planning: send offsets from caller counts, one block per sender.
 struct CountsArgs {
     Shape sh;
     Tables tb;
-    Outputs out;
     const int32_t* send_counts;
     uint32_t* status;
 };
@@ -240,52 +266,43 @@ struct CountsArgs {
 __global__ void __launch_bounds__(256) plan_from_counts_kernel(CountsArgs a) {
     __shared__ int sc[kMaxRanks + 1];
     __shared__ int wsum[5];
-    __shared__ int flag;
+    __shared__ int good;
     const int R = a.sh.R, tid = threadIdx.x, nt = blockDim.x, s = blockIdx.x;
     for (int d = tid; d < R; d += nt) sc[d] = a.send_counts[(int64_t)s * R + d];
     __syncthreads();
     if (tid == 0) {
+        // counts must be non-negative and fit the sender's rows (summed in 64 bits)
         int64_t sum = 0;
         bool ok = true;
-        for (int d = 0; d < R; ++d) { ok &= sc[d] >= 0; sum += sc[d]; }
-        flag = ok && sum <= a.sh.TK;
-        if (!flag) atomicOr(a.status, 1u);
+        for (int d = 0; d < R; ++d) { ok = ok && sc[d] >= 0; sum += sc[d]; }
+        good = ok && sum <= a.sh.TK;
+        if (!good) atomicOr(a.status, 1u);
     }
     __syncthreads();
-    if (!flag)
+    if (!good)
         for (int d = tid; d < R; d += nt) sc[d] = 0;
     __syncthreads();
     const int total = block_exclusive_scan(sc, R, wsum);
-    for (int d = tid; d <= R; d += nt) {
-        const int lo = d < R ? sc[d] : total;
-        a.tb.send_off[(int64_t)s * (R + 1) + d] = lo;
-        if (d < R) {
-            const int hi = d + 1 < R ? sc[d + 1] : total;
-            store_agent(a.tb.recv_counts + (int64_t)d * R + s, hi - lo);
-        }
-    }
-    if (!last_block_arrives(a.tb.ticket, &flag)) return;
-    finish_recv_tables(a.sh, a.tb, a.out, a.status);
-    if (tid == 0) __hip_atomic_store(a.tb.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int d = tid; d <= R; d += nt) a.tb.send_off[(int64_t)s * (R + 1) + d] = d < R ? sc[d] : total;
 }
 
 // ------------------------------------------------------------------------------------
 // Row movement.  One wavefront per row; lane l moves vectors l, l+64, ...; U vectors
-// per lane are loaded before any is stored, so a 10 KiB row is in flight at once.
+// per lane are loaded before any is stored.
 // ------------------------------------------------------------------------------------
-template <typename V, int U>
+template <typename V, int U, bool NT>
 __device__ __forceinline__ void copy_row(V* __restrict__ dst, const V* __restrict__ src, int nvec, int lane) {
     for (int base = 0; base < nvec; base += kWave * U) {
         V r[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int v = base + u * kWave + lane;
-            if (v < nvec) r[u] = src[v];
+            if (v < nvec) r[u] = ld<NT>(src + v);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int v = base + u * kWave + lane;
-            if (v < nvec) dst[v] = r[u];
+            if (v < nvec) st<NT>(dst + v, r[u]);
         }
     }
 }
@@ -306,62 +323,92 @@ __device__ __forceinline__ int segment_of(const int32_t* so, int R, int64_t p, i
     return d;
 }
 
-// pack: row x[s][t] to its k places in s's send buffer.
-template <typename V, int U>
-__global__ void __launch_bounds__(kBlock) pack_kernel(const V* __restrict__ x, V* __restrict__ send,
-                                                      const int32_t* __restrict__ pos, Shape sh, int nvec) {
+// pack: row x[s][t] to its k places: the sender's send buffer (staged) or the
+// receivers' buffers (direct).  The first blocks build the receive tables.
+template <typename V, int U, bool NT, bool DIRECT>
+__global__ void __launch_bounds__(kBlock) pack_kernel(const V* __restrict__ x, V* __restrict__ dst, Shape sh,
+                                                      Tables tb, Outputs out, uint32_t* status, int nvec) {
     const int lane = lane_id();
-    const int64_t n = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
+    const int64_t tblk = table_blocks(sh.R);
+    if ((int64_t)blockIdx.x < tblk) {
+        const int d = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
+        if (d < sh.R) write_recv_tables(sh, tb, out, status, d, lane);
+        return;
+    }
+    const int64_t n = ((int64_t)blockIdx.x - tblk) * kRowsPerBlock + threadIdx.x / kWave;
     if (n >= (int64_t)sh.R * sh.T) return;
     const int64_t s = n / sh.T;
     const int k = sh.k;
-    const int my = lane < k ? pos[n * k + lane] : -1;
+    const int R = sh.R;
+    const int my = lane < k ? tb.pos[n * k + lane] : -1;
     const V* src = x + n * nvec;
-    V* seg = send + s * sh.TK * nvec;
+    const int32_t* so = tb.send_off + s * (R + 1);
     for (int base = 0; base < nvec; base += kWave * U) {
         V r[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int v = base + u * kWave + lane;
-            if (v < nvec) r[u] = src[v];
+            if (v < nvec) r[u] = ld<NT>(src + v);
         }
         for (int j = 0; j < k; ++j) {
             const int pj = __builtin_amdgcn_readlane(my, j);
-            if (pj < 0 || pj >= sh.TK) continue;      // dropped slot (never out of the send buffer)
-            V* dst = seg + (int64_t)pj * nvec;
+            if (pj < 0 || pj >= sh.TK) continue;      // dropped slot (never out of the buffer)
+            V* row;
+            if constexpr (DIRECT) {
+                const int d = segment_of(so, R, pj, lane);
+                if (d >= R) continue;                   // not a sent row (tables always place it)
+                const int64_t q = recv_base(tb.send_off, R, d, (int)s, lane) + (pj - so[d]);
+                if (q < 0 || q >= sh.cap) continue;     // past the receiver's capacity (flagged)
+                row = dst + ((int64_t)d * sh.cap + q) * nvec;
+            } else {
+                row = dst + (s * sh.TK + pj) * nvec;
+            }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int v = base + u * kWave + lane;
-                if (v < nvec) dst[v] = r[u];
+                if (v < nvec) st<NT>(row + v, r[u]);
             }
         }
     }
 }
 
-// exchange: send row (s, p) <-> receive row (d, q).  Forward copies send -> recv and
-// drops rows past the capacity; reverse copies recv-layout expert outputs back to the
-// send places and writes zeros where a row was dropped.
-template <typename V, int U, bool REVERSE>
-__global__ void __launch_bounds__(kBlock) exchange_kernel(const V* __restrict__ src, V* __restrict__ dst,
-                                                          const int32_t* __restrict__ send_off,
-                                                          const int32_t* __restrict__ recv_off, Shape sh, int nvec) {
+// exchange (staged path): send row (s, p) <-> receive row (d, q).  Forward copies send
+// -> recv and drops rows past the capacity; reverse copies recv-layout expert outputs
+// back to the send places and writes zeros where a row was dropped.  FIRST: this is the
+// first kernel after planning (the bare collective), so the first blocks build the
+// receive tables and rows find their receive offset from the send offsets.
+template <typename V, int U, bool NT, bool REVERSE, bool FIRST>
+__global__ void __launch_bounds__(kBlock) exchange_kernel(const V* __restrict__ src, V* __restrict__ dst, Shape sh,
+                                                          Tables tb, Outputs out, uint32_t* status, int nvec) {
     const int lane = lane_id();
-    const int64_t g = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
+    int64_t blk = blockIdx.x;
+    if constexpr (FIRST) {
+        const int64_t tblk = table_blocks(sh.R);
+        if (blk < tblk) {
+            const int d = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
+            if (d < sh.R) write_recv_tables(sh, tb, out, status, d, lane);
+            return;
+        }
+        blk -= tblk;
+    }
+    const int64_t g = blk * kRowsPerBlock + threadIdx.x / kWave;
     if (g >= (int64_t)sh.R * sh.TK) return;
     const int R = sh.R;
     const int64_t s = g / sh.TK, p = g - s * sh.TK;
-    const int32_t* so = send_off + s * (R + 1);
+    const int32_t* so = tb.send_off + s * (R + 1);
     if (p >= so[R]) return;
     const int d = segment_of(so, R, p, lane);
-    const int64_t q = (int64_t)recv_off[(int64_t)d * (R + 1) + s] + (p - so[d]);
+    const int64_t base = FIRST ? recv_base(tb.send_off, R, d, (int)s, lane)
+                               : (int64_t)tb.recv_off[(int64_t)d * (R + 1) + s];
+    const int64_t q = base + (p - so[d]);
     const int64_t send_row = s * sh.TK + p, recv_row = (int64_t)d * sh.cap + q;
     const bool in_cap = q >= 0 && q < sh.cap;
     if (!REVERSE) {
         if (!in_cap) return;
-        copy_row<V, U>(dst + recv_row * nvec, src + send_row * nvec, nvec, lane);
+        copy_row<V, U, NT>(dst + recv_row * nvec, src + send_row * nvec, nvec, lane);
     } else {
         if (!in_cap) { zero_row<V>(dst + send_row * nvec, nvec, lane); return; }
-        copy_row<V, U>(dst + send_row * nvec, src + recv_row * nvec, nvec, lane);
+        copy_row<V, U, NT>(dst + send_row * nvec, src + recv_row * nvec, nvec, lane);
     }
 }
 
@@ -420,13 +467,14 @@ template <int B, int DT> struct Elems {
     }
 };
 
-// combine: y[s][t] = round(sum_j g_j * ret_s[pos_j]) with one float32 FMA per slot in
-// slot order, starting from 0.
-template <int B, int DT, int U>
-__global__ void __launch_bounds__(kBlock) combine_kernel(const typename Vec<B>::T* __restrict__ ret,
-                                                         const int32_t* __restrict__ pos,
+// combine: y[s][t] = round(sum_j g_j * row_j) with one float32 FMA per slot in slot
+// order, starting from 0.  row_j is the returned row at send place pos_j (staged) or
+// the expert output in the receiver's buffer (direct).
+template <int B, int DT, int U, bool NT, bool DIRECT>
+__global__ void __launch_bounds__(kBlock) combine_kernel(const typename Vec<B>::T* __restrict__ rows,
                                                          const float* __restrict__ gates,
-                                                         typename Vec<B>::T* __restrict__ y, Shape sh, int nvec) {
+                                                         typename Vec<B>::T* __restrict__ y, Shape sh, Tables tb,
+                                                         int nvec) {
     using V = typename Vec<B>::T;
     using El = Elems<B, DT>;
     constexpr int NE = El::N;
@@ -434,10 +482,25 @@ __global__ void __launch_bounds__(kBlock) combine_kernel(const typename Vec<B>::
     const int64_t n = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
     if (n >= (int64_t)sh.R * sh.T) return;
     const int64_t s = n / sh.T;
-    const int k = sh.k;
-    const int my_p = lane < k ? pos[n * k + lane] : -1;
+    const int k = sh.k, R = sh.R;
+    const int my_p = lane < k ? tb.pos[n * k + lane] : -1;
     const float my_g = lane < k ? gates[n * k + lane] : 0.0f;
-    const V* seg = ret + s * sh.TK * nvec;
+    // row index of each slot (held by lane j): a send place (staged) or a receive row
+    // (direct); -1 = the slot adds nothing
+    int64_t my_row = -1;
+    if constexpr (DIRECT) {
+        const int32_t* so = tb.send_off + s * (R + 1);
+        for (int j = 0; j < k; ++j) {
+            const int pj = __builtin_amdgcn_readlane(my_p, j);
+            if (pj < 0 || pj >= sh.TK) continue;
+            const int d = segment_of(so, R, pj, lane);
+            if (d >= R) continue;
+            const int64_t q = (int64_t)tb.recv_off[(int64_t)d * (R + 1) + s] + (pj - so[d]);
+            if (lane == j && q >= 0 && q < sh.cap) my_row = (int64_t)d * sh.cap + q;
+        }
+    } else {
+        if (my_p >= 0 && my_p < sh.TK) my_row = s * sh.TK + my_p;
+    }
     V* out = y + n * nvec;
     for (int base = 0; base < nvec; base += kWave * U) {
         float acc[U][NE];
@@ -446,15 +509,15 @@ __global__ void __launch_bounds__(kBlock) combine_kernel(const typename Vec<B>::
 #pragma unroll
             for (int e = 0; e < NE; ++e) acc[u][e] = 0.0f;
         for (int j = 0; j < k; ++j) {
-            const int pj = __builtin_amdgcn_readlane(my_p, j);
+            const int64_t rj = __shfl(my_row, j, kWave);
             const float gj = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_g), j));
-            if (pj < 0 || pj >= sh.TK) continue;      // dropped slot adds nothing
-            const V* row = seg + (int64_t)pj * nvec;
+            if (rj < 0) continue;                      // dropped slot adds nothing
+            const V* row = rows + rj * nvec;
             V r[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int v = base + u * kWave + lane;
-                if (v < nvec) r[u] = row[v];
+                if (v < nvec) r[u] = ld<NT>(row + v);
             }
 #pragma unroll
             for (int u = 0; u < U; ++u)
@@ -464,7 +527,7 @@ __global__ void __launch_bounds__(kBlock) combine_kernel(const typename Vec<B>::
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int v = base + u * kWave + lane;
-            if (v < nvec) out[v] = El::pack(acc[u]);
+            if (v < nvec) st<NT>(out + v, El::pack(acc[u]));
         }
     }
 }
@@ -475,10 +538,7 @@ __global__ void __launch_bounds__(kBlock) combine_kernel(const typename Vec<B>::
 // whose slice of the sender's expert-sorted segment holds it.
 template <int B, int DT, int U>
 __global__ void __launch_bounds__(kBlock) expert_kernel(const typename Vec<B>::T* __restrict__ in,
-                                                        typename Vec<B>::T* out,
-                                                        const int32_t* __restrict__ send_off,
-                                                        const int32_t* __restrict__ recv_off,
-                                                        const int32_t* __restrict__ cnt, Shape sh, int nvec,
+                                                        typename Vec<B>::T* out, Shape sh, Tables tb, int nvec,
                                                         int mode) {
     using V = typename Vec<B>::T;
     using El = Elems<B, DT>;
@@ -488,20 +548,20 @@ __global__ void __launch_bounds__(kBlock) expert_kernel(const typename Vec<B>::T
     if (g >= (int64_t)sh.R * sh.TK) return;
     const int R = sh.R;
     const int64_t s = g / sh.TK, p = g - s * sh.TK;
-    const int32_t* so = send_off + s * (R + 1);
+    const int32_t* so = tb.send_off + s * (R + 1);
     if (p >= so[R]) return;
     const int d = segment_of(so, R, p, lane);
     const int64_t i = p - so[d];
-    const int64_t q = (int64_t)recv_off[(int64_t)d * (R + 1) + s] + i;
+    const int64_t q = (int64_t)tb.recv_off[(int64_t)d * (R + 1) + s] + i;
     if (q < 0 || q >= sh.cap) return;
     const int64_t row = (int64_t)d * sh.cap + q;
     if (mode == 0) {
-        if (in != out) copy_row<V, U>(out + row * nvec, in + row * nvec, nvec, lane);
+        if (in != out) copy_row<V, U, false>(out + row * nvec, in + row * nvec, nvec, lane);
         return;
     }
     // local expert: number of the sender's per-expert counts for d whose running
     // sum is at or below i
-    const int32_t* c = cnt + s * sh.E + (int64_t)d * sh.epr;
+    const int32_t* c = tb.cnt + s * sh.E + (int64_t)d * sh.epr;
     int le = 0, carry = 0;
     for (int c0 = 0; c0 < sh.epr; c0 += kWave) {
         const int idx = c0 + lane;
@@ -539,6 +599,17 @@ __global__ void __launch_bounds__(1024) route_step_kernel(const int32_t* __restr
 // ---- launch helpers ------------------------------------------------------------------
 inline unsigned row_blocks(int64_t rows) { return (unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock); }
 
+// Non-temporal row traffic once a kernel's rows are far larger than the caches (the
+// 256 MiB last-level cache); small decode-sized steps keep rows cacheable so that the
+// next kernel can hit them.
+constexpr int64_t kStreamBytes = 256ll << 20;
+
+template <typename F>
+hipError_t with_nt(int64_t bytes, F&& f) {
+    if (bytes >= kStreamBytes) return f(std::true_type{});
+    return f(std::false_type{});
+}
+
 // Vectors per lane kept in flight: the smallest of 1, 2, 4, 8, 16 covering a row.
 template <typename F>
 hipError_t with_unroll(int nvec, F&& f) {
@@ -571,87 +642,121 @@ int pick_vec_bytes(int64_t row_bytes, const void* const* ptrs, int nptrs) {
     return 0;
 }
 
-hipError_t launch_plan(const Shape& sh, const Tables& tb, const int32_t* ids, const Outputs& out,
-                       uint32_t* status, hipStream_t st) {
-    // wavefronts per block: as many as fit (nw + 1) * E counters in 63 KiB (the
-    // kernel's static LDS takes the rest of 64 KiB), at most 16
-    const int nw = std::max(1, std::min(16, (int)(kPlanLdsBytes / (4 * (int64_t)sh.E)) - 1));
+int plan_waves(int32_t E) { return std::max(1, std::min(16, (int)(kPlanLdsBytes / (4 * (int64_t)E)) - 1)); }
+
+hipError_t launch_plan(const Shape& sh, const Tables& tb, const int32_t* ids, const Outputs& out, uint32_t* status,
+                       hipStream_t st) {
+    const int nw = plan_waves(sh.E);
     const size_t lds = (size_t)(nw + 1) * sh.E * sizeof(int);
     PlanArgs a{sh, tb, out, ids, status};
-    hipLaunchKernelGGL(plan_kernel, dim3(sh.R), dim3(nw * kWave), lds, st, a);
+    const int64_t per_wave = (sh.TK + nw - 1) / nw;
+    const int64_t slices = (per_wave + kWave - 1) / kWave;
+    if (slices <= 1) hipLaunchKernelGGL(plan_kernel<1>, dim3(sh.R), dim3(nw * kWave), lds, st, a);
+    else if (slices <= 2) hipLaunchKernelGGL(plan_kernel<2>, dim3(sh.R), dim3(nw * kWave), lds, st, a);
+    else if (slices <= 4) hipLaunchKernelGGL(plan_kernel<4>, dim3(sh.R), dim3(nw * kWave), lds, st, a);
+    else if (slices <= 8) hipLaunchKernelGGL(plan_kernel<8>, dim3(sh.R), dim3(nw * kWave), lds, st, a);
+    else hipLaunchKernelGGL(plan_kernel<16>, dim3(sh.R), dim3(nw * kWave), lds, st, a);
     return hipGetLastError();
 }
 
-hipError_t launch_plan_from_counts(const Shape& sh, const Tables& tb, const int32_t* send_counts,
-                                   const Outputs& out, uint32_t* status, hipStream_t st) {
-    CountsArgs a{sh, tb, out, send_counts, status};
+hipError_t launch_plan_from_counts(const Shape& sh, const Tables& tb, const int32_t* send_counts, uint32_t* status,
+                                   hipStream_t st) {
+    CountsArgs a{sh, tb, send_counts, status};
     hipLaunchKernelGGL(plan_from_counts_kernel, dim3(sh.R), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
-hipError_t launch_pack(const Shape& sh, const Tables& tb, const void* x, void* send, int vec, hipStream_t st) {
+hipError_t launch_pack(const Shape& sh, const Tables& tb, const Outputs& out, uint32_t* status, const void* x,
+                       void* dst, bool direct, int vec, hipStream_t st) {
     const int64_t N = (int64_t)sh.R * sh.T;
-    if (N == 0) return hipSuccess;
     const int nvec = (int)(sh.row_bytes / vec);
+    const unsigned grid = (unsigned)(table_blocks(sh.R) + row_blocks(N));
+    const int64_t bytes = N * sh.row_bytes;
     return with_vec(vec, [&](auto B) {
         using V = typename Vec<decltype(B)::value>::T;
         return with_unroll(nvec, [&](auto U) {
-            hipLaunchKernelGGL((pack_kernel<V, decltype(U)::value>), dim3(row_blocks(N)), dim3(kBlock), 0, st,
-                               (const V*)x, (V*)send, tb.pos, sh, nvec);
-            return hipGetLastError();
+            return with_nt(bytes, [&](auto NT) {
+                constexpr int u = decltype(U)::value;
+                constexpr bool nt = decltype(NT)::value;
+                if (direct)
+                    hipLaunchKernelGGL((pack_kernel<V, u, nt, true>), dim3(grid), dim3(kBlock), 0, st, (const V*)x,
+                                       (V*)dst, sh, tb, out, status, nvec);
+                else
+                    hipLaunchKernelGGL((pack_kernel<V, u, nt, false>), dim3(grid), dim3(kBlock), 0, st, (const V*)x,
+                                       (V*)dst, sh, tb, out, status, nvec);
+                return hipGetLastError();
+            });
         });
     });
 }
 
-hipError_t launch_exchange(const Shape& sh, const Tables& tb, const void* src, void* dst, bool reverse, int vec,
-                           hipStream_t st) {
+hipError_t launch_exchange(const Shape& sh, const Tables& tb, const Outputs& out, uint32_t* status, const void* src,
+                           void* dst, bool reverse, bool first, int vec, hipStream_t st) {
     const int64_t rows = (int64_t)sh.R * sh.TK;
-    if (rows == 0) return hipSuccess;
     const int nvec = (int)(sh.row_bytes / vec);
+    const unsigned grid = (unsigned)((first ? table_blocks(sh.R) : 0) + row_blocks(rows));
+    if (grid == 0) return hipSuccess;
+    const int64_t bytes = rows * sh.row_bytes;
     return with_vec(vec, [&](auto B) {
         using V = typename Vec<decltype(B)::value>::T;
         return with_unroll(nvec, [&](auto U) {
-            if (reverse)
-                hipLaunchKernelGGL((exchange_kernel<V, decltype(U)::value, true>), dim3(row_blocks(rows)),
-                                   dim3(kBlock), 0, st, (const V*)src, (V*)dst, tb.send_off, tb.recv_off, sh, nvec);
-            else
-                hipLaunchKernelGGL((exchange_kernel<V, decltype(U)::value, false>), dim3(row_blocks(rows)),
-                                   dim3(kBlock), 0, st, (const V*)src, (V*)dst, tb.send_off, tb.recv_off, sh, nvec);
-            return hipGetLastError();
+            return with_nt(bytes, [&](auto NT) {
+                constexpr int u = decltype(U)::value;
+                constexpr bool nt = decltype(NT)::value;
+                if (first)
+                    hipLaunchKernelGGL((exchange_kernel<V, u, nt, false, true>), dim3(grid), dim3(kBlock), 0, st,
+                                       (const V*)src, (V*)dst, sh, tb, out, status, nvec);
+                else if (reverse)
+                    hipLaunchKernelGGL((exchange_kernel<V, u, nt, true, false>), dim3(grid), dim3(kBlock), 0, st,
+                                       (const V*)src, (V*)dst, sh, tb, out, status, nvec);
+                else
+                    hipLaunchKernelGGL((exchange_kernel<V, u, nt, false, false>), dim3(grid), dim3(kBlock), 0, st,
+                                       (const V*)src, (V*)dst, sh, tb, out, status, nvec);
+                return hipGetLastError();
+            });
         });
     });
 }
 
 template <int B, int DT>
-static hipError_t launch_combine_t(const Shape& sh, const Tables& tb, const void* ret, const float* gates, void* y,
-                                   hipStream_t st) {
+static hipError_t launch_combine_t(const Shape& sh, const Tables& tb, const void* rows, const float* gates, void* y,
+                                   bool direct, hipStream_t st) {
     using V = typename Vec<B>::T;
     const int nvec = (int)(sh.row_bytes / B);
     const int64_t N = (int64_t)sh.R * sh.T;
+    const int64_t bytes = N * sh.row_bytes;
     return with_unroll(nvec, [&](auto U) {
-        // keep float accumulators within a sane register budget
-        constexpr int UU = (decltype(U)::value * Elems<B, DT>::N > 64) ? 64 / Elems<B, DT>::N : decltype(U)::value;
-        hipLaunchKernelGGL((combine_kernel<B, DT, UU>), dim3(row_blocks(N)), dim3(kBlock), 0, st, (const V*)ret,
-                           tb.pos, gates, (V*)y, sh, nvec);
-        return hipGetLastError();
+        return with_nt(bytes, [&](auto NT) {
+            // keep float accumulators within a sane register budget
+            constexpr int UU = (decltype(U)::value * Elems<B, DT>::N > 64) ? 64 / Elems<B, DT>::N
+                                                                            : decltype(U)::value;
+            constexpr bool nt = decltype(NT)::value;
+            if (direct)
+                hipLaunchKernelGGL((combine_kernel<B, DT, UU, nt, true>), dim3(row_blocks(N)), dim3(kBlock), 0, st,
+                                   (const V*)rows, gates, (V*)y, sh, tb, nvec);
+            else
+                hipLaunchKernelGGL((combine_kernel<B, DT, UU, nt, false>), dim3(row_blocks(N)), dim3(kBlock), 0, st,
+                                   (const V*)rows, gates, (V*)y, sh, tb, nvec);
+            return hipGetLastError();
+        });
     });
 }
 
-hipError_t launch_combine(const Shape& sh, const Tables& tb, const void* ret, const float* gates, void* y, int vec,
-                          hipStream_t st) {
+hipError_t launch_combine(const Shape& sh, const Tables& tb, const void* rows, const float* gates, void* y, bool direct,
+                          int vec, hipStream_t st) {
     if ((int64_t)sh.R * sh.T == 0) return hipSuccess;
     if (sh.dtype == 1) {
         switch (vec) {
-            case 16: return launch_combine_t<16, 1>(sh, tb, ret, gates, y, st);
-            case 8: return launch_combine_t<8, 1>(sh, tb, ret, gates, y, st);
-            case 4: return launch_combine_t<4, 1>(sh, tb, ret, gates, y, st);
-            default: return launch_combine_t<2, 1>(sh, tb, ret, gates, y, st);
+            case 16: return launch_combine_t<16, 1>(sh, tb, rows, gates, y, direct, st);
+            case 8: return launch_combine_t<8, 1>(sh, tb, rows, gates, y, direct, st);
+            case 4: return launch_combine_t<4, 1>(sh, tb, rows, gates, y, direct, st);
+            default: return launch_combine_t<2, 1>(sh, tb, rows, gates, y, direct, st);
         }
     }
     switch (vec) {
-        case 16: return launch_combine_t<16, 0>(sh, tb, ret, gates, y, st);
-        case 8: return launch_combine_t<8, 0>(sh, tb, ret, gates, y, st);
-        default: return launch_combine_t<4, 0>(sh, tb, ret, gates, y, st);
+        case 16: return launch_combine_t<16, 0>(sh, tb, rows, gates, y, direct, st);
+        case 8: return launch_combine_t<8, 0>(sh, tb, rows, gates, y, direct, st);
+        default: return launch_combine_t<4, 0>(sh, tb, rows, gates, y, direct, st);
     }
 }
 
@@ -663,7 +768,7 @@ static hipError_t launch_expert_t(const Shape& sh, const Tables& tb, const void*
     const int64_t rows = (int64_t)sh.R * sh.TK;
     return with_unroll(nvec, [&](auto U) {
         hipLaunchKernelGGL((expert_kernel<B, DT, decltype(U)::value>), dim3(row_blocks(rows)), dim3(kBlock), 0, st,
-                           (const V*)in, (V*)out, tb.send_off, tb.recv_off, tb.cnt, sh, nvec, mode);
+                           (const V*)in, (V*)out, sh, tb, nvec, mode);
         return hipGetLastError();
     });
 }

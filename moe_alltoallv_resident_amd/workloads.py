@@ -71,12 +71,6 @@ class Workload:
             return self.recv_capacity_rows
         return self.num_ranks * self.tokens_per_rank * min(self.top_k, self.experts_per_rank)
 
-    def staged_bytes(self) -> int:
-        """Algorithmic HBM bytes of one staged dispatch+combine over real rows:
-        pack reads N rows and writes A, the exchange reads and writes A, the return
-        reads and writes A, the combine reads A and writes N: (2N + 6A) rows."""
-        return (2 * self.tokens + 6 * self.assignments) * self.row_bytes
-
     def describe(self) -> str:
         return (f"{self.name}: R{self.num_ranks} T{self.tokens_per_rank} H{self.hidden} "
                 f"{DTYPE_NAMES[self.dtype]} E{self.num_experts} top{self.top_k} {self.routing}"

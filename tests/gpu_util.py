@@ -76,11 +76,11 @@ class Run:
     """One dispatch -> expert stand-in -> combine pass of the HIP path, step by step,
     with the tables and rows copied to the host for comparison."""
 
-    def __init__(self, w: W.Workload, x, ids, gates, session=None):
+    def __init__(self, w: W.Workload, x, ids, gates, session=None, path=a2av.PATH_STAGED, device_inputs=None):
         self.w = w
-        self.x_dev, self.ids_dev, self.gates_dev = to_device(w, x, ids, gates)
+        self.x_dev, self.ids_dev, self.gates_dev = device_inputs or to_device(w, x, ids, gates)
         self.session = session or a2av.Session(w.num_ranks, w.tokens_per_rank, w.hidden, w.dtype,
-                                               w.experts_per_rank, w.top_k, w.recv_capacity_rows)
+                                               w.experts_per_rank, w.top_k, w.recv_capacity_rows, path=path)
         self.recv = self.z = None
 
     def dispatch(self, keep_recv=True):

@@ -41,7 +41,7 @@ def test_error_strings():
 @pytest.mark.parametrize("bad", [
     dict(num_ranks=0), dict(num_ranks=2000), dict(tokens_per_rank=-1), dict(hidden=0), dict(dtype=7),
     dict(experts_per_rank=0), dict(experts_per_rank=513), dict(top_k=0), dict(top_k=65),
-    dict(num_ranks=2, experts_per_rank=1, top_k=3), dict(recv_capacity_rows=-5),
+    dict(num_ranks=2, experts_per_rank=1, top_k=3), dict(recv_capacity_rows=-5), dict(path=2),
 ])
 def test_workspace_bytes_rejects_invalid_configs(bad):
     base = dict(num_ranks=8, tokens_per_rank=128, hidden=5120, dtype=a2av.BF16, experts_per_rank=16, top_k=1)
@@ -54,3 +54,6 @@ def test_workspace_bytes_counts_send_buffer_and_tables():
     n = a2av.a2av_workspace_bytes(a2av.make_config(R, T, H, a2av.BF16, epr, k))
     send = R * T * k * H * 2
     assert send < n < send + 4 * 1024 * 1024
+    # the direct path has no send buffer
+    nd = a2av.a2av_workspace_bytes(a2av.make_config(R, T, H, a2av.BF16, epr, k, path=a2av.PATH_DIRECT))
+    assert 0 < nd < 4 * 1024 * 1024

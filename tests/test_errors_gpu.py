@@ -16,9 +16,9 @@ from tests.gpu_util import assert_combine_close, banner, host_bits, to_device
 pytestmark = pytest.mark.gpu
 
 
-def _cfg(w):
+def _cfg(w, path=a2av.PATH_STAGED):
     return a2av.make_config(w.num_ranks, w.tokens_per_rank, w.hidden, w.dtype, w.experts_per_rank, w.top_k,
-                            w.recv_capacity_rows)
+                            w.recv_capacity_rows, path)
 
 
 def test_host_side_rejections_enqueue_nothing():
@@ -50,14 +50,16 @@ def test_host_side_rejections_enqueue_nothing():
     torch.cuda.synchronize()
     assert int(st.item()) == 0
     a2av.a2av_destroy(h)
-    # invalid configuration
-    bad = _cfg(w)
-    bad.top_k = 99
-    with pytest.raises(a2av.A2AVError):
-        a2av.a2av_create(bad)
+    # invalid configurations
+    for field, value in (("top_k", 99), ("path", 5), ("reserved", 1)):
+        bad = _cfg(w)
+        setattr(bad, field, value)
+        with pytest.raises(a2av.A2AVError):
+            a2av.a2av_create(bad)
 
 
-def test_receive_overflow_keeps_guard_rows_and_true_counts():
+@pytest.mark.parametrize("path", [a2av.PATH_STAGED, a2av.PATH_DIRECT], ids=["staged", "direct"])
+def test_receive_overflow_keeps_guard_rows_and_true_counts(path):
     w = W.workload("wide", num_ranks=4, tokens_per_rank=64, hidden=96, experts_per_rank=2, top_k=2)
     x, ids, gates = W.make_inputs(w)
     full = oracle.dispatch(oracle.as_rows(x), ids, w.experts_per_rank, w.capacity)
@@ -74,7 +76,7 @@ def test_receive_overflow_keeps_guard_rows_and_true_counts():
     rc = torch.empty((R, R), dtype=torch.int32, device="cuda")
     ro = torch.empty((R, R + 1), dtype=torch.int32, device="cuda")
     st = torch.zeros(1, dtype=torch.int32, device="cuda")
-    h = a2av.a2av_create(_cfg(w))
+    h = a2av.a2av_create(_cfg(w, path))
     a2av.a2av_dispatch(h, xt, idt, recv, split, rc, ro, st)
     torch.cuda.synchronize()
     assert int(st.item()) == a2av.ST_RECV_OVERFLOW
@@ -146,9 +148,10 @@ def test_bare_alltoallv_matches_oracle_exchange():
     a2av.a2av_destroy(h)
 
 
-def test_zero_tokens():
+@pytest.mark.parametrize("path", [a2av.PATH_STAGED, a2av.PATH_DIRECT], ids=["staged", "direct"])
+def test_zero_tokens(path):
     w = W.workload("decode", tokens_per_rank=0)
-    h = a2av.a2av_create(_cfg(w))
+    h = a2av.a2av_create(_cfg(w, path))
     R = w.num_ranks
     split = torch.full((R, w.num_experts), 5, dtype=torch.int32, device="cuda")
     rc = torch.full((R, R), 5, dtype=torch.int32, device="cuda")

@@ -29,10 +29,11 @@ def _tables(w, steps):
     return ids, gates
 
 
+@pytest.mark.parametrize("path", [a2av.PATH_STAGED, a2av.PATH_DIRECT], ids=["staged", "direct"])
 @pytest.mark.parametrize("name,steps,full_every", [("decode", 100, 10), ("edge", 24, 1)])
-def test_graph_replay_with_device_side_routing(name, steps, full_every):
+def test_graph_replay_with_device_side_routing(name, steps, full_every, path):
     w = W.workload(name)
-    banner(f"graph replay {w.describe()} steps={steps}")
+    banner(f"graph replay {w.describe()} steps={steps} path={path}")
     x = W.make_x(w)
     ids_tab, gates_tab = _tables(w, steps)
     xt, _, _ = to_device(w, x, ids_tab[0], gates_tab[0])
@@ -43,7 +44,7 @@ def test_graph_replay_with_device_side_routing(name, steps, full_every):
     ids = torch.empty((w.num_ranks, w.tokens_per_rank, w.top_k), dtype=torch.int32, device="cuda")
     gates = torch.empty((w.num_ranks, w.tokens_per_rank, w.top_k), dtype=torch.float32, device="cuda")
     y = torch.empty_like(xt)
-    s = a2av.Session(w.num_ranks, w.tokens_per_rank, w.hidden, w.dtype, w.experts_per_rank, w.top_k)
+    s = a2av.Session(w.num_ranks, w.tokens_per_rank, w.hidden, w.dtype, w.experts_per_rank, w.top_k, path=path)
 
     def step():
         a2av.a2av_route_step(ids_table, gates_table, steps, n, counter, ids, gates)

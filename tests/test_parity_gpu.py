@@ -17,7 +17,7 @@ import oracle
 from moe_alltoallv_resident_amd import a2av
 from moe_alltoallv_resident_amd import workloads as W
 from tests.gpu_util import (Run, assert_combine_close, assert_tables_equal, banner, host_bits,
-                            oracle_tables)
+                            oracle_tables, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -27,10 +27,14 @@ def _free():
     torch.cuda.empty_cache()
 
 
-def _full_oracle_check(w: W.Workload, x, ids, gates, run: Run = None):
-    banner(f"full check {w.describe()} cap={w.capacity}")
+PATHS = [a2av.PATH_STAGED, a2av.PATH_DIRECT]
+PATH_IDS = ["staged", "direct"]
+
+
+def _full_oracle_check(w: W.Workload, x, ids, gates, path=a2av.PATH_STAGED):
+    banner(f"full check {w.describe()} cap={w.capacity} path={PATH_IDS[path]}")
     ref = oracle.full_step(x, ids, gates, w.experts_per_rank, w.dtype, w.expert_mode, w.capacity)
-    run = run or Run(w, x, ids, gates).all()
+    run = Run(w, x, ids, gates, path=path).all()
     R = w.num_ranks
     assert_tables_equal(run, ref, R)
     assert run.status == ref["status"], (run.status, ref["status"])
@@ -84,37 +88,42 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
 @pytest.mark.parametrize("name,over", SMALL, ids=[f"{n}-{i}" for i, (n, _) in enumerate(SMALL)])
-def test_small_and_ragged_cases_match_oracle(name, over):
+def test_small_and_ragged_cases_match_oracle(name, over, path):
     w = W.workload(name, **over)
     x, ids, gates = W.make_inputs(w)
-    ref = _full_oracle_check(w, x, ids, gates)
+    ref = _full_oracle_check(w, x, ids, gates, path)
     if over.get("recv_capacity_rows"):
         assert ref["status"] & oracle.ST_RECV_OVERFLOW
 
 
-def test_repeated_ids_within_a_token_are_sent_k_times():
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
+def test_repeated_ids_within_a_token_are_sent_k_times(path):
     w = W.workload("tiny", num_ranks=3, tokens_per_rank=50, hidden=32, experts_per_rank=2, top_k=3)
     x, _, gates = W.make_inputs(w)
     ids = np.random.default_rng(9).integers(0, w.num_experts, size=(3, 50, 3)).astype(np.int32)
-    _full_oracle_check(w, x, ids, gates)
+    _full_oracle_check(w, x, ids, gates, path)
 
 
-def test_out_of_range_ids_are_dropped_and_flagged():
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
+def test_out_of_range_ids_are_dropped_and_flagged(path):
     w = W.workload("wide", num_ranks=4, tokens_per_rank=24, hidden=128, experts_per_rank=4, top_k=2)
     x, ids, gates = W.make_inputs(w)
     ids = ids.copy()
     ids[0, 3, 1] = w.num_experts
     ids[2, 0, 0] = -1
     ids[3, 23, 1] = 1 << 30
-    ref = _full_oracle_check(w, x, ids, gates)
+    ref = _full_oracle_check(w, x, ids, gates, path)
     assert ref["status"] == oracle.ST_EXPERT_RANGE
 
 
-def test_decode_steps_with_fresh_routing():
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
+def test_decode_steps_with_fresh_routing(path):
     w = W.workload("decode")
     x = W.make_x(w)
-    session = a2av.Session(w.num_ranks, w.tokens_per_rank, w.hidden, w.dtype, w.experts_per_rank, w.top_k)
+    session = a2av.Session(w.num_ranks, w.tokens_per_rank, w.hidden, w.dtype, w.experts_per_rank, w.top_k,
+                           path=path)
     for step in range(3):
         ids, gates = W.make_ids(w, step), W.make_gates(w, step)
         run = Run(w, x, ids, gates, session=session).all()
@@ -154,40 +163,45 @@ def test_full_size_workload(name):
     banner(f"full size {w.describe()} cap={w.capacity}")
     x, ids, gates = W.make_inputs(w)
     ref = oracle_tables(w, ids)
-    run = Run(w, x, ids, gates).dispatch(keep_recv=False)
-    assert_tables_equal(run, ref, w.num_ranks)
-    assert run.session.status.item() == 0
-
-    # every receive row equals the input row its oracle tag names
-    s = run.session
-    xf = run.x_dev.reshape(w.tokens, w.hidden)
-    for d in range(w.num_ranks):
-        n = run.valid[d]
-        if n == 0:
-            continue
-        tags = torch.from_numpy(ref["recv_tags"][d, :n].astype(np.int64)).cuda()
-        assert torch.equal(s.recv[d, :n], xf.index_select(0, tags)), f"receive rows of rank {d}"
-    banner("  receive rows bit-exact")
-    run.expert(keep_z=False).combine()
-    assert run.status == 0
-
-    # combine on sampled token ranges against the oracle's closed form
     rng = np.random.default_rng(17)
     budget = {"prefill": 4096, "wide": 1024}.get(name, w.tokens)
     span = min(budget, 256) if budget < w.tokens else w.tokens
     starts = [0] if span == w.tokens else sorted(
         set([0, w.tokens - span] + list(rng.integers(0, w.tokens - span, budget // span - 2))))
-    y_host = run.y.reshape(w.tokens, w.hidden)
-    checked = 0
-    for a in starts:
-        yref = oracle.closed_form(x, ids, gates, w.experts_per_rank, w.dtype, w.expert_mode, a, a + span)
-        assert_combine_close(y_host[a:a + span], yref.reshape(span, w.hidden), w.dtype, f"{name} tokens {a}+{span}")
-        checked += span
-    banner(f"  combine matches the oracle on {checked} sampled tokens")
+    yrefs = {a: oracle.closed_form(x, ids, gates, w.experts_per_rank, w.dtype, w.expert_mode, a, a + span)
+             for a in starts}
+    dev = to_device(w, x, ids, gates)
+    yt = None
+    for path, pname in zip(PATHS, PATH_IDS):
+        banner(f"  path {pname}")
+        run = Run(w, x, ids, gates, path=path, device_inputs=dev).dispatch(keep_recv=False)
+        assert_tables_equal(run, ref, w.num_ranks)
+        assert run.session.status.item() == 0
 
-    # every token: the same definition in float32 torch arithmetic
-    yt = _torch_definition_f32(w, run.x_dev, run.ids_dev, run.gates_dev)
-    assert_combine_close(run.y, host_bits(yt), w.dtype, f"{name} torch float32 definition")
-    s.close()
-    del run, s, yt
-    _free()
+        # every receive row equals the input row its oracle tag names
+        s = run.session
+        xf = run.x_dev.reshape(w.tokens, w.hidden)
+        for d in range(w.num_ranks):
+            n = run.valid[d]
+            if n == 0:
+                continue
+            tags = torch.from_numpy(ref["recv_tags"][d, :n].astype(np.int64)).cuda()
+            assert torch.equal(s.recv[d, :n], xf.index_select(0, tags)), f"receive rows of rank {d}"
+        banner("    receive rows bit-exact")
+        run.expert(keep_z=False).combine()
+        assert run.status == 0
+
+        # combine on sampled token ranges against the oracle's closed form
+        y_host = run.y.reshape(w.tokens, w.hidden)
+        for a in starts:
+            assert_combine_close(y_host[a:a + span], yrefs[a].reshape(span, w.hidden), w.dtype,
+                                 f"{name} {pname} tokens {a}+{span}")
+        banner(f"    combine matches the oracle on {len(starts) * span} sampled tokens")
+
+        # every token: the same definition in float32 torch arithmetic
+        if yt is None:
+            yt = host_bits(_torch_definition_f32(w, run.x_dev, run.ids_dev, run.gates_dev))
+        assert_combine_close(run.y, yt, w.dtype, f"{name} {pname} torch float32 definition")
+        s.close()
+        del run, s
+        _free()
