@@ -71,6 +71,7 @@ bool make_shape(const a2av_config_t* c, Shape* sh) {
     sh->TK = TK;
     sh->cap = cap;
     sh->row_bytes = (int64_t)c->hidden * (c->dtype == A2AV_BF16 ? 2 : 4);
+    sh->num_cu = 256;
     return true;
 }
 
@@ -159,7 +160,11 @@ int a2av_create(const a2av_config_t* cfg, a2av_handle_t* out) {
     h->cfg = *cfg;
     h->sh = sh;
     h->direct = cfg->path == A2AV_PATH_DIRECT;
-    if (hipGetDevice(&h->device) != hipSuccess) { delete h; return A2AV_ERR_HIP; }
+    if (hipGetDevice(&h->device) != hipSuccess ||
+        hipDeviceGetAttribute(&h->sh.num_cu, hipDeviceAttributeMultiprocessorCount, h->device) != hipSuccess) {
+        delete h;
+        return A2AV_ERR_HIP;
+    }
     const MetaLayout m = meta_layout(sh);
     const size_t sb = std::max<size_t>(send_bytes(cfg, sh), kAlign);
     if (hipMalloc(&h->send_buf, sb) != hipSuccess) { (void)hipGetLastError(); delete h; return A2AV_ERR_NOMEM; }

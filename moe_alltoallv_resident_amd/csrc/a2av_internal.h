@@ -19,6 +19,7 @@ struct Shape {
     int64_t TK;         // T * k, send rows per rank
     int64_t cap;        // receive rows per rank
     int64_t row_bytes;  // H * element bytes
+    int32_t num_cu;     // compute units of the device (sizes row splitting)
 };
 
 // Device tables in the handle's workspace (rank-major, int32 rows).

@@ -39,6 +39,15 @@ template <> struct Vec<8> { using T = u32x2; };
 template <> struct Vec<4> { using T = uint32_t; };
 template <> struct Vec<2> { using T = uint16_t; };
 
+// How rows are cut into chunks, one wavefront per chunk: when a kernel has too few rows
+// to give every CU several wavefronts (decode sizes), each row is split into cpr chunks
+// of cv vectors (a multiple of 64, so every lane moves the same count); otherwise cpr = 1.
+struct Split {
+    int nvec;   // vectors per row
+    int cpr;    // chunks per row
+    int cv;     // vectors per chunk
+};
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
 __device__ __forceinline__ uint64_t lanes_below(int lane) {
@@ -290,26 +299,41 @@ __global__ void __launch_bounds__(256) plan_from_counts_kernel(CountsArgs a) {
 // Row movement.  One wavefront per row; lane l moves vectors l, l+64, ...; U vectors
 // per lane are loaded before any is stored.
 // ------------------------------------------------------------------------------------
+// Copy vectors [v0, v1) of a row.
 template <typename V, int U, bool NT>
-__device__ __forceinline__ void copy_row(V* __restrict__ dst, const V* __restrict__ src, int nvec, int lane) {
-    for (int base = 0; base < nvec; base += kWave * U) {
+__device__ __forceinline__ void copy_row(V* __restrict__ dst, const V* __restrict__ src, int v0, int v1, int lane) {
+    for (int base = v0; base < v1; base += kWave * U) {
         V r[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int v = base + u * kWave + lane;
-            if (v < nvec) r[u] = ld<NT>(src + v);
+            if (v < v1) r[u] = ld<NT>(src + v);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int v = base + u * kWave + lane;
-            if (v < nvec) st<NT>(dst + v, r[u]);
+            if (v < v1) st<NT>(dst + v, r[u]);
         }
     }
 }
 
 template <typename V>
-__device__ __forceinline__ void zero_row(V* __restrict__ dst, int nvec, int lane) {
-    for (int v = lane; v < nvec; v += kWave) dst[v] = V{};
+__device__ __forceinline__ void zero_row(V* __restrict__ dst, int v0, int v1, int lane) {
+    for (int v = v0 + lane; v < v1; v += kWave) dst[v] = V{};
+}
+
+// The wavefront's (row, chunk) and its vector range.
+struct Piece {
+    int64_t row;
+    int v0, v1;
+};
+__device__ __forceinline__ Piece piece_of(int64_t wave, const Split& sp) {
+    Piece p;
+    p.row = wave / sp.cpr;
+    const int c = (int)(wave - p.row * sp.cpr);
+    p.v0 = c * sp.cv;
+    p.v1 = min(sp.nvec, p.v0 + sp.cv);
+    return p;
 }
 
 // Which destination segment holds send row p of a sender: the number of segment ends
@@ -327,7 +351,7 @@ __device__ __forceinline__ int segment_of(const int32_t* so, int R, int64_t p, i
 // receivers' buffers (direct).  The first blocks build the receive tables.
 template <typename V, int U, bool NT, bool DIRECT>
 __global__ void __launch_bounds__(kBlock) pack_kernel(const V* __restrict__ x, V* __restrict__ dst, Shape sh,
-                                                      Tables tb, Outputs out, uint32_t* status, int nvec) {
+                                                      Tables tb, Outputs out, uint32_t* status, Split sp) {
     const int lane = lane_id();
     const int64_t tblk = table_blocks(sh.R);
     if ((int64_t)blockIdx.x < tblk) {
@@ -335,20 +359,22 @@ __global__ void __launch_bounds__(kBlock) pack_kernel(const V* __restrict__ x, V
         if (d < sh.R) write_recv_tables(sh, tb, out, status, d, lane);
         return;
     }
-    const int64_t n = ((int64_t)blockIdx.x - tblk) * kRowsPerBlock + threadIdx.x / kWave;
+    const Piece pc = piece_of(((int64_t)blockIdx.x - tblk) * kRowsPerBlock + threadIdx.x / kWave, sp);
+    const int64_t n = pc.row;
     if (n >= (int64_t)sh.R * sh.T) return;
     const int64_t s = n / sh.T;
     const int k = sh.k;
     const int R = sh.R;
+    const int nvec = sp.nvec;
     const int my = lane < k ? tb.pos[n * k + lane] : -1;
     const V* src = x + n * nvec;
     const int32_t* so = tb.send_off + s * (R + 1);
-    for (int base = 0; base < nvec; base += kWave * U) {
+    for (int base = pc.v0; base < pc.v1; base += kWave * U) {
         V r[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int v = base + u * kWave + lane;
-            if (v < nvec) r[u] = ld<NT>(src + v);
+            if (v < pc.v1) r[u] = ld<NT>(src + v);
         }
         for (int j = 0; j < k; ++j) {
             const int pj = __builtin_amdgcn_readlane(my, j);
@@ -366,7 +392,7 @@ __global__ void __launch_bounds__(kBlock) pack_kernel(const V* __restrict__ x, V
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int v = base + u * kWave + lane;
-                if (v < nvec) st<NT>(row + v, r[u]);
+                if (v < pc.v1) st<NT>(row + v, r[u]);
             }
         }
     }
@@ -379,7 +405,7 @@ __global__ void __launch_bounds__(kBlock) pack_kernel(const V* __restrict__ x, V
 // receive tables and rows find their receive offset from the send offsets.
 template <typename V, int U, bool NT, bool REVERSE, bool FIRST>
 __global__ void __launch_bounds__(kBlock) exchange_kernel(const V* __restrict__ src, V* __restrict__ dst, Shape sh,
-                                                          Tables tb, Outputs out, uint32_t* status, int nvec) {
+                                                          Tables tb, Outputs out, uint32_t* status, Split sp) {
     const int lane = lane_id();
     int64_t blk = blockIdx.x;
     if constexpr (FIRST) {
@@ -391,9 +417,11 @@ __global__ void __launch_bounds__(kBlock) exchange_kernel(const V* __restrict__ 
         }
         blk -= tblk;
     }
-    const int64_t g = blk * kRowsPerBlock + threadIdx.x / kWave;
+    const Piece pc = piece_of(blk * kRowsPerBlock + threadIdx.x / kWave, sp);
+    const int64_t g = pc.row;
     if (g >= (int64_t)sh.R * sh.TK) return;
     const int R = sh.R;
+    const int nvec = sp.nvec;
     const int64_t s = g / sh.TK, p = g - s * sh.TK;
     const int32_t* so = tb.send_off + s * (R + 1);
     if (p >= so[R]) return;
@@ -405,10 +433,10 @@ __global__ void __launch_bounds__(kBlock) exchange_kernel(const V* __restrict__ 
     const bool in_cap = q >= 0 && q < sh.cap;
     if (!REVERSE) {
         if (!in_cap) return;
-        copy_row<V, U, NT>(dst + recv_row * nvec, src + send_row * nvec, nvec, lane);
+        copy_row<V, U, NT>(dst + recv_row * nvec, src + send_row * nvec, pc.v0, pc.v1, lane);
     } else {
-        if (!in_cap) { zero_row<V>(dst + send_row * nvec, nvec, lane); return; }
-        copy_row<V, U, NT>(dst + send_row * nvec, src + recv_row * nvec, nvec, lane);
+        if (!in_cap) { zero_row<V>(dst + send_row * nvec, pc.v0, pc.v1, lane); return; }
+        copy_row<V, U, NT>(dst + send_row * nvec, src + recv_row * nvec, pc.v0, pc.v1, lane);
     }
 }
 
@@ -474,15 +502,17 @@ template <int B, int DT, int U, bool NT, bool DIRECT>
 __global__ void __launch_bounds__(kBlock) combine_kernel(const typename Vec<B>::T* __restrict__ rows,
                                                          const float* __restrict__ gates,
                                                          typename Vec<B>::T* __restrict__ y, Shape sh, Tables tb,
-                                                         int nvec) {
+                                                         Split sp) {
     using V = typename Vec<B>::T;
     using El = Elems<B, DT>;
     constexpr int NE = El::N;
     const int lane = lane_id();
-    const int64_t n = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
+    const Piece pc = piece_of((int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kWave, sp);
+    const int64_t n = pc.row;
     if (n >= (int64_t)sh.R * sh.T) return;
     const int64_t s = n / sh.T;
     const int k = sh.k, R = sh.R;
+    const int nvec = sp.nvec;
     const int my_p = lane < k ? tb.pos[n * k + lane] : -1;
     const float my_g = lane < k ? gates[n * k + lane] : 0.0f;
     // row index of each slot (held by lane j): a send place (staged) or a receive row
@@ -502,7 +532,7 @@ __global__ void __launch_bounds__(kBlock) combine_kernel(const typename Vec<B>::
         if (my_p >= 0 && my_p < sh.TK) my_row = s * sh.TK + my_p;
     }
     V* out = y + n * nvec;
-    for (int base = 0; base < nvec; base += kWave * U) {
+    for (int base = pc.v0; base < pc.v1; base += kWave * U) {
         float acc[U][NE];
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -517,7 +547,7 @@ __global__ void __launch_bounds__(kBlock) combine_kernel(const typename Vec<B>::
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int v = base + u * kWave + lane;
-                if (v < nvec) r[u] = ld<NT>(row + v);
+                if (v < pc.v1) r[u] = ld<NT>(row + v);
             }
 #pragma unroll
             for (int u = 0; u < U; ++u)
@@ -527,7 +557,7 @@ __global__ void __launch_bounds__(kBlock) combine_kernel(const typename Vec<B>::
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int v = base + u * kWave + lane;
-            if (v < nvec) st<NT>(out + v, El::pack(acc[u]));
+            if (v < pc.v1) st<NT>(out + v, El::pack(acc[u]));
         }
     }
 }
@@ -538,15 +568,17 @@ __global__ void __launch_bounds__(kBlock) combine_kernel(const typename Vec<B>::
 // whose slice of the sender's expert-sorted segment holds it.
 template <int B, int DT, int U>
 __global__ void __launch_bounds__(kBlock) expert_kernel(const typename Vec<B>::T* __restrict__ in,
-                                                        typename Vec<B>::T* out, Shape sh, Tables tb, int nvec,
+                                                        typename Vec<B>::T* out, Shape sh, Tables tb, Split sp,
                                                         int mode) {
     using V = typename Vec<B>::T;
     using El = Elems<B, DT>;
     constexpr int NE = El::N;
     const int lane = lane_id();
-    const int64_t g = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
+    const Piece pc = piece_of((int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kWave, sp);
+    const int64_t g = pc.row;
     if (g >= (int64_t)sh.R * sh.TK) return;
     const int R = sh.R;
+    const int nvec = sp.nvec;
     const int64_t s = g / sh.TK, p = g - s * sh.TK;
     const int32_t* so = tb.send_off + s * (R + 1);
     if (p >= so[R]) return;
@@ -556,7 +588,7 @@ __global__ void __launch_bounds__(kBlock) expert_kernel(const typename Vec<B>::T
     if (q < 0 || q >= sh.cap) return;
     const int64_t row = (int64_t)d * sh.cap + q;
     if (mode == 0) {
-        if (in != out) copy_row<V, U, false>(out + row * nvec, in + row * nvec, nvec, lane);
+        if (in != out) copy_row<V, U, false>(out + row * nvec, in + row * nvec, pc.v0, pc.v1, lane);
         return;
     }
     // local expert: number of the sender's per-expert counts for d whose running
@@ -573,7 +605,7 @@ __global__ void __launch_bounds__(kBlock) expert_kernel(const typename Vec<B>::T
     const float scale = 1.0f + (float)(d * sh.epr + le) / 256.0f;
     const V* src = in + row * nvec;
     V* dst = out + row * nvec;
-    for (int v = lane; v < nvec; v += kWave) {
+    for (int v = pc.v0 + lane; v < pc.v1; v += kWave) {
         const V r = src[v];
         float f[NE];
 #pragma unroll
@@ -610,7 +642,28 @@ hipError_t with_nt(int64_t bytes, F&& f) {
     return f(std::false_type{});
 }
 
-// Vectors per lane kept in flight: the smallest of 1, 2, 4, 8, 16 covering a row.
+// Wavefronts a row kernel should have to keep every CU busy on short grids.
+constexpr int kWavesPerCu = 16;
+
+Split make_split(int64_t row_bytes, int vec, int64_t rows, int num_cu) {
+    Split sp;
+    sp.nvec = (int)(row_bytes / vec);
+    int cpr = 1;
+    if (rows > 0) {
+        const int64_t target = (int64_t)num_cu * kWavesPerCu;
+        cpr = (int)std::min<int64_t>((target + rows - 1) / rows, std::max(1, sp.nvec / kWave));
+        cpr = std::max(1, cpr);
+    }
+    int cv = (sp.nvec + cpr - 1) / cpr;
+    if (cpr > 1) cv = (cv + kWave - 1) / kWave * kWave;
+    sp.cv = cv;
+    sp.cpr = (sp.nvec + cv - 1) / cv;
+    return sp;
+}
+
+inline unsigned piece_blocks(int64_t rows, const Split& sp) { return row_blocks(rows * sp.cpr); }
+
+// Vectors per lane kept in flight: the smallest of 1, 2, 4, 8, 16 covering a chunk.
 template <typename F>
 hipError_t with_unroll(int nvec, F&& f) {
     const int per_lane = (nvec + kWave - 1) / kWave;
@@ -669,21 +722,21 @@ hipError_t launch_plan_from_counts(const Shape& sh, const Tables& tb, const int3
 hipError_t launch_pack(const Shape& sh, const Tables& tb, const Outputs& out, uint32_t* status, const void* x,
                        void* dst, bool direct, int vec, hipStream_t st) {
     const int64_t N = (int64_t)sh.R * sh.T;
-    const int nvec = (int)(sh.row_bytes / vec);
-    const unsigned grid = (unsigned)(table_blocks(sh.R) + row_blocks(N));
+    const Split sp = make_split(sh.row_bytes, vec, N, sh.num_cu);
+    const unsigned grid = (unsigned)(table_blocks(sh.R) + piece_blocks(N, sp));
     const int64_t bytes = N * sh.row_bytes;
     return with_vec(vec, [&](auto B) {
         using V = typename Vec<decltype(B)::value>::T;
-        return with_unroll(nvec, [&](auto U) {
+        return with_unroll(sp.cv, [&](auto U) {
             return with_nt(bytes, [&](auto NT) {
                 constexpr int u = decltype(U)::value;
                 constexpr bool nt = decltype(NT)::value;
                 if (direct)
                     hipLaunchKernelGGL((pack_kernel<V, u, nt, true>), dim3(grid), dim3(kBlock), 0, st, (const V*)x,
-                                       (V*)dst, sh, tb, out, status, nvec);
+                                       (V*)dst, sh, tb, out, status, sp);
                 else
                     hipLaunchKernelGGL((pack_kernel<V, u, nt, false>), dim3(grid), dim3(kBlock), 0, st, (const V*)x,
-                                       (V*)dst, sh, tb, out, status, nvec);
+                                       (V*)dst, sh, tb, out, status, sp);
                 return hipGetLastError();
             });
         });
@@ -693,25 +746,25 @@ hipError_t launch_pack(const Shape& sh, const Tables& tb, const Outputs& out, ui
 hipError_t launch_exchange(const Shape& sh, const Tables& tb, const Outputs& out, uint32_t* status, const void* src,
                            void* dst, bool reverse, bool first, int vec, hipStream_t st) {
     const int64_t rows = (int64_t)sh.R * sh.TK;
-    const int nvec = (int)(sh.row_bytes / vec);
-    const unsigned grid = (unsigned)((first ? table_blocks(sh.R) : 0) + row_blocks(rows));
+    const Split sp = make_split(sh.row_bytes, vec, rows, sh.num_cu);
+    const unsigned grid = (unsigned)((first ? table_blocks(sh.R) : 0) + piece_blocks(rows, sp));
     if (grid == 0) return hipSuccess;
     const int64_t bytes = rows * sh.row_bytes;
     return with_vec(vec, [&](auto B) {
         using V = typename Vec<decltype(B)::value>::T;
-        return with_unroll(nvec, [&](auto U) {
+        return with_unroll(sp.cv, [&](auto U) {
             return with_nt(bytes, [&](auto NT) {
                 constexpr int u = decltype(U)::value;
                 constexpr bool nt = decltype(NT)::value;
                 if (first)
                     hipLaunchKernelGGL((exchange_kernel<V, u, nt, false, true>), dim3(grid), dim3(kBlock), 0, st,
-                                       (const V*)src, (V*)dst, sh, tb, out, status, nvec);
+                                       (const V*)src, (V*)dst, sh, tb, out, status, sp);
                 else if (reverse)
                     hipLaunchKernelGGL((exchange_kernel<V, u, nt, true, false>), dim3(grid), dim3(kBlock), 0, st,
-                                       (const V*)src, (V*)dst, sh, tb, out, status, nvec);
+                                       (const V*)src, (V*)dst, sh, tb, out, status, sp);
                 else
                     hipLaunchKernelGGL((exchange_kernel<V, u, nt, false, false>), dim3(grid), dim3(kBlock), 0, st,
-                                       (const V*)src, (V*)dst, sh, tb, out, status, nvec);
+                                       (const V*)src, (V*)dst, sh, tb, out, status, sp);
                 return hipGetLastError();
             });
         });
@@ -722,21 +775,21 @@ template <int B, int DT>
 static hipError_t launch_combine_t(const Shape& sh, const Tables& tb, const void* rows, const float* gates, void* y,
                                    bool direct, hipStream_t st) {
     using V = typename Vec<B>::T;
-    const int nvec = (int)(sh.row_bytes / B);
     const int64_t N = (int64_t)sh.R * sh.T;
+    const Split sp = make_split(sh.row_bytes, B, N, sh.num_cu);
     const int64_t bytes = N * sh.row_bytes;
-    return with_unroll(nvec, [&](auto U) {
+    return with_unroll(sp.cv, [&](auto U) {
         return with_nt(bytes, [&](auto NT) {
             // keep float accumulators within a sane register budget
             constexpr int UU = (decltype(U)::value * Elems<B, DT>::N > 64) ? 64 / Elems<B, DT>::N
                                                                             : decltype(U)::value;
             constexpr bool nt = decltype(NT)::value;
             if (direct)
-                hipLaunchKernelGGL((combine_kernel<B, DT, UU, nt, true>), dim3(row_blocks(N)), dim3(kBlock), 0, st,
-                                   (const V*)rows, gates, (V*)y, sh, tb, nvec);
+                hipLaunchKernelGGL((combine_kernel<B, DT, UU, nt, true>), dim3(piece_blocks(N, sp)), dim3(kBlock), 0,
+                                   st, (const V*)rows, gates, (V*)y, sh, tb, sp);
             else
-                hipLaunchKernelGGL((combine_kernel<B, DT, UU, nt, false>), dim3(row_blocks(N)), dim3(kBlock), 0, st,
-                                   (const V*)rows, gates, (V*)y, sh, tb, nvec);
+                hipLaunchKernelGGL((combine_kernel<B, DT, UU, nt, false>), dim3(piece_blocks(N, sp)), dim3(kBlock), 0,
+                                   st, (const V*)rows, gates, (V*)y, sh, tb, sp);
             return hipGetLastError();
         });
     });
@@ -764,11 +817,11 @@ template <int B, int DT>
 static hipError_t launch_expert_t(const Shape& sh, const Tables& tb, const void* in, void* out, int mode,
                                   hipStream_t st) {
     using V = typename Vec<B>::T;
-    const int nvec = (int)(sh.row_bytes / B);
     const int64_t rows = (int64_t)sh.R * sh.TK;
-    return with_unroll(nvec, [&](auto U) {
-        hipLaunchKernelGGL((expert_kernel<B, DT, decltype(U)::value>), dim3(row_blocks(rows)), dim3(kBlock), 0, st,
-                           (const V*)in, (V*)out, sh, tb, nvec, mode);
+    const Split sp = make_split(sh.row_bytes, B, rows, sh.num_cu);
+    return with_unroll(sp.cv, [&](auto U) {
+        hipLaunchKernelGGL((expert_kernel<B, DT, decltype(U)::value>), dim3(piece_blocks(rows, sp)), dim3(kBlock), 0,
+                           st, (const V*)in, (V*)out, sh, tb, sp, mode);
         return hipGetLastError();
     });
 }
