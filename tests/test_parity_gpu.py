@@ -85,6 +85,9 @@ SMALL = [
     # a small receive capacity (rows dropped, flagged, counts kept)
     ("wide", dict(num_ranks=4, tokens_per_rank=30, hidden=64, experts_per_rank=2, top_k=2,
                   recv_capacity_rows=20)),
+    # more assignments per wavefront than its registers hold: planning in several batches
+    ("wide", dict(num_ranks=2, tokens_per_rank=9000, hidden=16, experts_per_rank=8, top_k=2)),
+    ("wide", dict(num_ranks=8, tokens_per_rank=2000, hidden=16, experts_per_rank=512, top_k=4)),
 ]
 
 
@@ -96,6 +99,28 @@ def test_small_and_ragged_cases_match_oracle(name, over, path):
     ref = _full_oracle_check(w, x, ids, gates, path)
     if over.get("recv_capacity_rows"):
         assert ref["status"] & oracle.ST_RECV_OVERFLOW
+
+
+def _random_case(i):
+    rng = np.random.default_rng(1000 + i)
+    R = int(rng.choice([1, 2, 3, 5, 8, 13, 16, 31, 64]))
+    epr = int(rng.choice([1, 2, 3, 7, 16]))
+    E = R * epr
+    k = int(rng.integers(1, min(E, 8) + 1))
+    T = int(rng.choice([0, 1, 7, 33, 100, 257]))
+    dtype = int(rng.choice([W.F32, W.BF16]))
+    H = int(rng.choice([1, 3, 8, 64, 99, 100, 640, 1000]))
+    routing = "zipf" if (k == 1 and rng.random() < 0.5) else "uniform"
+    return W.Workload(f"random{i}", R, T, H, dtype, epr, k, routing, str(rng.choice(["softmax", "sigmoid"])),
+                      int(rng.integers(0, 2)), zipf_s=1.2, seed=i)
+
+
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
+@pytest.mark.parametrize("i", range(12))
+def test_seeded_random_shapes_match_oracle(i, path):
+    w = _random_case(i)
+    x, ids, gates = W.make_inputs(w)
+    _full_oracle_check(w, x, ids, gates, path)
 
 
 @pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
