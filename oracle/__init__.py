@@ -21,6 +21,8 @@ F32 = 0
 BF16 = 1
 ST_EXPERT_RANGE = 1
 ST_RECV_OVERFLOW = 2
+SOURCE_MAJOR = 0
+EXPERT_MAJOR = 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liba2av_oracle.so")
@@ -35,9 +37,9 @@ def _load():
             _b.build()
         lib = ctypes.CDLL(_LIB_PATH)
         i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
-        lib.oracle_dispatch.argtypes = [i32, i32, i32, i32, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
-        lib.oracle_expert.argtypes = [i32, i32, i64, i32, i64, i32, vp, vp, vp, vp]
-        lib.oracle_return.argtypes = [i32, i32, i32, i64, i64, vp, vp, vp, vp]
+        lib.oracle_dispatch.argtypes = [i32, i32, i32, i32, i64, i64, i32] + [vp] * 11
+        lib.oracle_expert.argtypes = [i32, i32, i64, i32, i64, i32, i32, vp, vp, vp, vp]
+        lib.oracle_return.argtypes = [i32, i32, i32, i32, i64, i64, i32, vp, vp, vp, vp, vp]
         lib.oracle_combine.argtypes = [i32, i32, i32, i64, i32, vp, vp, vp, vp]
         lib.oracle_closed_form.argtypes = [i32, i32, i32, i32, i64, i32, i32, vp, vp, vp, vp, i64, i64]
         lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
@@ -70,12 +72,13 @@ def as_rows(x: np.ndarray) -> np.ndarray:
     return x.view(np.uint8).reshape(x.shape[:-1] + (x.shape[-1] * x.itemsize,))
 
 
-def dispatch(x_rows: np.ndarray, ids: np.ndarray, experts_per_rank: int, cap: int):
+def dispatch(x_rows: np.ndarray, ids: np.ndarray, experts_per_rank: int, cap: int, layout: int = SOURCE_MAJOR):
     """Sort by expert into send buffers, then the all-to-allv.
 
     x_rows: [R][T][row_bytes] uint8 (see ``as_rows``); ids: [R][T][k] int32.
     Returns a dict with cnt [R][E], send_off [R][R+1], pos [R][T][k], send [R][T*k][row],
-    recv_counts [R][R] ([dst][src]), recv_off [R][R+1], recv [R][cap][row], status.
+    recv_counts [R][R] ([dst][src]), recv_off [R][R+1], recv_eoff [R][epr+1],
+    recv [R][cap][row] (source- or expert-major), status.
     """
     x_rows = _c(x_rows, np.uint8)
     ids = _c(ids, np.int32)
@@ -90,12 +93,14 @@ def dispatch(x_rows: np.ndarray, ids: np.ndarray, experts_per_rank: int, cap: in
         send=np.zeros((R, T * k, row), np.uint8),
         recv_counts=np.zeros((R, R), np.int32),
         recv_off=np.zeros((R, R + 1), np.int32),
+        recv_eoff=np.zeros((R, experts_per_rank + 1), np.int32),
         recv=np.zeros((R, cap, row), np.uint8),
     )
     st = np.zeros(1, np.uint32)
-    rc = _load().oracle_dispatch(R, T, k, experts_per_rank, row, cap, _p(x_rows), _p(ids),
+    rc = _load().oracle_dispatch(R, T, k, experts_per_rank, row, cap, layout, _p(x_rows), _p(ids),
                                  _p(out["cnt"]), _p(out["send_off"]), _p(out["pos"]), _p(out["send"]),
-                                 _p(out["recv_counts"]), _p(out["recv_off"]), _p(out["recv"]), _p(st))
+                                 _p(out["recv_counts"]), _p(out["recv_off"]), _p(out["recv_eoff"]),
+                                 _p(out["recv"]), _p(st))
     if rc != 0:
         raise ValueError("oracle_dispatch rejected its arguments")
     out["status"] = int(st[0])
@@ -103,7 +108,7 @@ def dispatch(x_rows: np.ndarray, ids: np.ndarray, experts_per_rank: int, cap: in
 
 
 def expert(recv: np.ndarray, cnt: np.ndarray, recv_off: np.ndarray, experts_per_rank: int,
-           dtype: int, mode: int) -> np.ndarray:
+           dtype: int, mode: int, layout: int = SOURCE_MAJOR) -> np.ndarray:
     """Expert stand-in on received rows: mode 0 identity, mode 1 scale by 1 + e/256.
 
     recv: [R][cap][H] float32 or uint16 (bf16 bits).  Returns z of the same shape.
@@ -111,20 +116,24 @@ def expert(recv: np.ndarray, cnt: np.ndarray, recv_off: np.ndarray, experts_per_
     recv = np.ascontiguousarray(recv)
     R, cap, H = recv.shape
     z = np.zeros_like(recv)
-    rc = _load().oracle_expert(R, experts_per_rank, H, dtype, cap, mode,
+    rc = _load().oracle_expert(R, experts_per_rank, H, dtype, cap, mode, layout,
                                _p(_c(cnt, np.int32)), _p(_c(recv_off, np.int32)), _p(recv), _p(z))
     if rc != 0:
         raise ValueError("oracle_expert rejected its arguments")
     return z
 
 
-def return_exchange(z_rows: np.ndarray, send_off: np.ndarray, recv_off: np.ndarray, T: int, k: int) -> np.ndarray:
-    """Return all-to-all.  z_rows: [R][cap][row] uint8.  Returns ret [R][T*k][row] uint8."""
+def return_exchange(z_rows: np.ndarray, send_off: np.ndarray, recv_off: np.ndarray, T: int, k: int,
+                    cnt: np.ndarray = None, experts_per_rank: int = 1, layout: int = SOURCE_MAJOR) -> np.ndarray:
+    """Return all-to-all.  z_rows: [R][cap][row] uint8.  Returns ret [R][T*k][row] uint8.
+    The expert-major layout needs the split table cnt [R][E]."""
     z_rows = _c(z_rows, np.uint8)
     R, cap, row = z_rows.shape
+    if cnt is None:
+        cnt = np.zeros((R, R * experts_per_rank), np.int32)
     ret = np.zeros((R, T * k, row), np.uint8)
-    rc = _load().oracle_return(R, T, k, row, cap, _p(_c(send_off, np.int32)), _p(_c(recv_off, np.int32)),
-                               _p(z_rows), _p(ret))
+    rc = _load().oracle_return(R, T, k, experts_per_rank, row, cap, layout, _p(_c(cnt, np.int32)),
+                               _p(_c(send_off, np.int32)), _p(_c(recv_off, np.int32)), _p(z_rows), _p(ret))
     if rc != 0:
         raise ValueError("oracle_return rejected its arguments")
     return ret
@@ -170,15 +179,15 @@ def closed_form(x: np.ndarray, ids: np.ndarray, gates: np.ndarray, experts_per_r
 
 
 def full_step(x: np.ndarray, ids: np.ndarray, gates: np.ndarray, experts_per_rank: int, dtype: int,
-              mode: int, cap: int):
+              mode: int, cap: int, layout: int = SOURCE_MAJOR):
     """dispatch -> expert stand-in -> return -> combine, the whole staged path on the CPU."""
     x = np.ascontiguousarray(x)
-    d = dispatch(as_rows(x), ids, experts_per_rank, cap)
+    d = dispatch(as_rows(x), ids, experts_per_rank, cap, layout)
     R, T, H = x.shape
     k = ids.shape[2]
     recv = d["recv"].view(x.dtype).reshape(R, cap, H)
-    z = expert(recv, d["cnt"], d["recv_off"], experts_per_rank, dtype, mode)
-    ret = return_exchange(as_rows(z), d["send_off"], d["recv_off"], T, k)
+    z = expert(recv, d["cnt"], d["recv_off"], experts_per_rank, dtype, mode, layout)
+    ret = return_exchange(as_rows(z), d["send_off"], d["recv_off"], T, k, d["cnt"], experts_per_rank, layout)
     y = combine(ret.view(x.dtype).reshape(R, T * k, H), d["pos"], gates, dtype)
     d.update(recv=recv, z=z, ret=ret.view(x.dtype).reshape(R, T * k, H), y=y)
     return d

@@ -30,7 +30,11 @@
  *   - expert e lives on rank owner(e) = e / experts_per_rank (contiguous blocks);
  *   - "sorted by expert" is a stable sort by (expert, token, slot);
  *   - a receive buffer is laid out source-major (rows from rank 0 first), keeping the
- *     sender's order inside each source segment, as any all-to-allv does;
+ *     sender's order inside each source segment, as any all-to-allv does; the
+ *     expert-major layout (an option) groups a receiver's rows by its local expert,
+ *     then by source rank, then in the sender's order, which is the grouping an
+ *     expert's computation right after the dispatch wants (abhik.ai page, Figure 13:
+ *     tokens travel to the GPU that holds their expert);
  *   - counts and offsets are in rows (int32);
  *   - a token whose k experts share a rank is sent k times (no de-duplication);
  *   - an expert id outside [0, E) is dropped (status bit 1), and its slot adds
@@ -57,6 +61,18 @@
 
 #define ORACLE_ST_EXPERT_RANGE  1u
 #define ORACLE_ST_RECV_OVERFLOW 2u
+
+#define ORACLE_LAYOUT_SOURCE_MAJOR 0
+#define ORACLE_LAYOUT_EXPERT_MAJOR 1
+
+/* First place of expert e's rows in sender s's expert-sorted order: the rows s sends
+ * to experts below e. */
+static int64_t sender_expert_start(const int32_t* cnt, int32_t E, int32_t s, int32_t e)
+{
+    int64_t run = 0;
+    for (int32_t e2 = 0; e2 < e; ++e2) run += cnt[(int64_t)s * E + e2];
+    return run;
+}
 
 /* ---------------------------------------------------------------------------------
  * Number formats.  bf16 is the upper half of an IEEE binary32: 1 sign bit, 8 exponent
@@ -135,16 +151,21 @@ static int64_t elem_bytes(int dtype) { return dtype == ORACLE_BF16 ? 2 : 4; }
  *   send     [R][T*k][row_bytes] out  send buffers (expert-sorted)
  *   recv_counts [R][R] out       recv_counts[d][s] = rows rank d receives from rank s
  *   recv_off [R][R+1]  out       exclusive prefix of recv_counts[d][.] over s
- *   recv     [R][cap][row_bytes] out  receive buffers; rows past the received count untouched
+ *   recv_eoff [R][epr+1] out     rows rank d receives for its local experts below le
+ *                                (exclusive prefix; where expert groups start in the
+ *                                expert-major layout)
+ *   recv     [R][cap][row_bytes] out  receive buffers (layout: source- or expert-major);
+ *                                rows past the received count untouched
  *   status   out                 OR of ORACLE_ST_* bits
  * Returns 0, or -1 for unusable arguments.
  * ------------------------------------------------------------------------------- */
-int oracle_dispatch(int32_t R, int32_t T, int32_t k, int32_t epr, int64_t row_bytes, int64_t cap,
+int oracle_dispatch(int32_t R, int32_t T, int32_t k, int32_t epr, int64_t row_bytes, int64_t cap, int32_t layout,
                     const uint8_t* x, const int32_t* ids,
                     int32_t* cnt, int32_t* send_off, int32_t* pos, uint8_t* send,
-                    int32_t* recv_counts, int32_t* recv_off, uint8_t* recv, uint32_t* status)
+                    int32_t* recv_counts, int32_t* recv_off, int32_t* recv_eoff, uint8_t* recv, uint32_t* status)
 {
     if (R < 1 || T < 0 || k < 1 || epr < 1 || row_bytes < 1 || cap < 0) return -1;
+    if (layout != ORACLE_LAYOUT_SOURCE_MAJOR && layout != ORACLE_LAYOUT_EXPERT_MAJOR) return -1;
     const int32_t E = R * epr;
     const int64_t TK = (int64_t)T * k;
     uint32_t st = 0;
@@ -202,14 +223,40 @@ int oracle_dispatch(int32_t R, int32_t T, int32_t k, int32_t epr, int64_t row_by
         recv_off[(int64_t)d * (R + 1) + R] = run;
     }
     for (int32_t d = 0; d < R; ++d) {
-        for (int32_t s = 0; s < R; ++s) {
-            int32_t c = recv_counts[(int64_t)d * R + s];
-            for (int32_t i = 0; i < c; ++i) {
-                int64_t q = (int64_t)recv_off[(int64_t)d * (R + 1) + s] + i;
-                int64_t p = (int64_t)send_off[(int64_t)s * (R + 1) + d] + i;
-                if (q >= cap) { st |= ORACLE_ST_RECV_OVERFLOW; continue; }
-                memcpy(recv + ((int64_t)d * cap + q) * row_bytes,
-                       send + ((int64_t)s * TK + p) * row_bytes, (size_t)row_bytes);
+        int32_t run = 0;
+        for (int32_t le = 0; le < epr; ++le) {
+            recv_eoff[(int64_t)d * (epr + 1) + le] = run;
+            for (int32_t s = 0; s < R; ++s) run += cnt[(int64_t)s * E + d * epr + le];
+        }
+        recv_eoff[(int64_t)d * (epr + 1) + epr] = run;
+    }
+    for (int32_t d = 0; d < R; ++d) {
+        if (layout == ORACLE_LAYOUT_SOURCE_MAJOR) {
+            /* segment from s = 0 first, each segment in the sender's order */
+            for (int32_t s = 0; s < R; ++s) {
+                int32_t c = recv_counts[(int64_t)d * R + s];
+                for (int32_t i = 0; i < c; ++i) {
+                    int64_t q = (int64_t)recv_off[(int64_t)d * (R + 1) + s] + i;
+                    int64_t p = (int64_t)send_off[(int64_t)s * (R + 1) + d] + i;
+                    if (q >= cap) { st |= ORACLE_ST_RECV_OVERFLOW; continue; }
+                    memcpy(recv + ((int64_t)d * cap + q) * row_bytes,
+                           send + ((int64_t)s * TK + p) * row_bytes, (size_t)row_bytes);
+                }
+            }
+        } else {
+            /* local expert 0 first; inside an expert, source 0 first; inside a source,
+             * the sender's order */
+            int64_t q = 0;
+            for (int32_t le = 0; le < epr; ++le) {
+                int32_t e = d * epr + le;
+                for (int32_t s = 0; s < R; ++s) {
+                    int64_t p0 = sender_expert_start(cnt, E, s, e);
+                    for (int32_t i = 0; i < cnt[(int64_t)s * E + e]; ++i, ++q) {
+                        if (q >= cap) { st |= ORACLE_ST_RECV_OVERFLOW; continue; }
+                        memcpy(recv + ((int64_t)d * cap + q) * row_bytes,
+                               send + ((int64_t)s * TK + p0 + i) * row_bytes, (size_t)row_bytes);
+                    }
+                }
             }
         }
     }
@@ -225,20 +272,25 @@ int oracle_dispatch(int32_t R, int32_t T, int32_t k, int32_t epr, int64_t row_by
  *   recv, z  [R][cap][H] of dtype; only the first min(recv_off[d][R], cap) rows of
  *   each rank are read and written.
  * ------------------------------------------------------------------------------- */
-int oracle_expert(int32_t R, int32_t epr, int64_t H, int32_t dtype, int64_t cap, int32_t mode,
+int oracle_expert(int32_t R, int32_t epr, int64_t H, int32_t dtype, int64_t cap, int32_t mode, int32_t layout,
                   const int32_t* cnt, const int32_t* recv_off,
                   const uint8_t* recv, uint8_t* z)
 {
     if (R < 1 || epr < 1 || H < 1 || cap < 0 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16)) return -1;
+    if (layout != ORACLE_LAYOUT_SOURCE_MAJOR && layout != ORACLE_LAYOUT_EXPERT_MAJOR) return -1;
     const int32_t E = R * epr;
     const int64_t rb = H * elem_bytes(dtype);
     for (int32_t d = 0; d < R; ++d) {
-        for (int32_t s = 0; s < R; ++s) {
-            int64_t q = recv_off[(int64_t)d * (R + 1) + s];
-            for (int32_t le = 0; le < epr; ++le) {
+        int64_t q = 0;
+        /* visit the received rows of d in their layout's order, with their expert */
+        for (int32_t outer = 0; outer < (layout == ORACLE_LAYOUT_SOURCE_MAJOR ? R : epr); ++outer) {
+            for (int32_t inner = 0; inner < (layout == ORACLE_LAYOUT_SOURCE_MAJOR ? epr : R); ++inner) {
+                int32_t s = layout == ORACLE_LAYOUT_SOURCE_MAJOR ? outer : inner;
+                int32_t le = layout == ORACLE_LAYOUT_SOURCE_MAJOR ? inner : outer;
                 int32_t e = d * epr + le;
                 int32_t c = cnt[(int64_t)s * E + e];
                 double scale = 1.0 + (double)e / 256.0;
+                if (layout == ORACLE_LAYOUT_SOURCE_MAJOR && le == 0) q = recv_off[(int64_t)d * (R + 1) + s];
                 for (int32_t i = 0; i < c; ++i, ++q) {
                     if (q >= cap) continue;
                     const uint8_t* in = recv + ((int64_t)d * cap + q) * rb;
@@ -254,26 +306,47 @@ int oracle_expert(int32_t R, int32_t epr, int64_t H, int32_t dtype, int64_t cap,
 }
 
 /* ---------------------------------------------------------------------------------
- * Return all-to-all: the inverse of the exchange.  Row i of the segment d received
- * from s goes back to place send_off[s][d] + i of s's return buffer.  A row that was
+ * Return all-to-all: the inverse of the exchange.  Every received row goes back to the
+ * place its row had in the sender's send order (source-major: row i of the segment d
+ * received from s goes to place send_off[s][d] + i; expert-major: row i of the block
+ * of expert e from s goes to the sender's first place for e plus i).  A row that was
  * dropped for lack of capacity comes back as zeros.
  *   z   [R][cap][row_bytes];  ret [R][T*k][row_bytes]
  * ------------------------------------------------------------------------------- */
-int oracle_return(int32_t R, int32_t T, int32_t k, int64_t row_bytes, int64_t cap,
-                  const int32_t* send_off, const int32_t* recv_off,
+int oracle_return(int32_t R, int32_t T, int32_t k, int32_t epr, int64_t row_bytes, int64_t cap, int32_t layout,
+                  const int32_t* cnt, const int32_t* send_off, const int32_t* recv_off,
                   const uint8_t* z, uint8_t* ret)
 {
-    if (R < 1 || T < 0 || k < 1 || row_bytes < 1 || cap < 0) return -1;
+    if (R < 1 || T < 0 || k < 1 || epr < 1 || row_bytes < 1 || cap < 0) return -1;
+    if (layout != ORACLE_LAYOUT_SOURCE_MAJOR && layout != ORACLE_LAYOUT_EXPERT_MAJOR) return -1;
     const int64_t TK = (int64_t)T * k;
-    for (int32_t s = 0; s < R; ++s) {
-        for (int32_t d = 0; d < R; ++d) {
-            int64_t p0 = send_off[(int64_t)s * (R + 1) + d];
-            int64_t c = send_off[(int64_t)s * (R + 1) + d + 1] - p0;
-            int64_t q0 = recv_off[(int64_t)d * (R + 1) + s];
-            for (int64_t i = 0; i < c; ++i) {
-                uint8_t* out = ret + ((int64_t)s * TK + p0 + i) * row_bytes;
-                if (q0 + i >= cap) { memset(out, 0, (size_t)row_bytes); continue; }
-                memcpy(out, z + ((int64_t)d * cap + q0 + i) * row_bytes, (size_t)row_bytes);
+    const int32_t E = R * epr;
+    if (layout == ORACLE_LAYOUT_SOURCE_MAJOR) {
+        for (int32_t s = 0; s < R; ++s) {
+            for (int32_t d = 0; d < R; ++d) {
+                int64_t p0 = send_off[(int64_t)s * (R + 1) + d];
+                int64_t c = send_off[(int64_t)s * (R + 1) + d + 1] - p0;
+                int64_t q0 = recv_off[(int64_t)d * (R + 1) + s];
+                for (int64_t i = 0; i < c; ++i) {
+                    uint8_t* out = ret + ((int64_t)s * TK + p0 + i) * row_bytes;
+                    if (q0 + i >= cap) { memset(out, 0, (size_t)row_bytes); continue; }
+                    memcpy(out, z + ((int64_t)d * cap + q0 + i) * row_bytes, (size_t)row_bytes);
+                }
+            }
+        }
+        return 0;
+    }
+    for (int32_t d = 0; d < R; ++d) {
+        int64_t q = 0;
+        for (int32_t le = 0; le < epr; ++le) {
+            int32_t e = d * epr + le;
+            for (int32_t s = 0; s < R; ++s) {
+                int64_t p0 = sender_expert_start(cnt, E, s, e);
+                for (int32_t i = 0; i < cnt[(int64_t)s * E + e]; ++i, ++q) {
+                    uint8_t* out = ret + ((int64_t)s * TK + p0 + i) * row_bytes;
+                    if (q >= cap) { memset(out, 0, (size_t)row_bytes); continue; }
+                    memcpy(out, z + ((int64_t)d * cap + q) * row_bytes, (size_t)row_bytes);
+                }
             }
         }
     }

@@ -44,3 +44,19 @@ def recv_lists(ids, R, T, k, epr):
                             lst.append((s, t, j, e))
         out.append(lst)
     return out
+
+
+def recv_lists_expert_major(ids, R, T, k, epr):
+    """recv[d] in the expert-major layout: for each destination d, each expert e of d,
+    each source s, each token t, slot j."""
+    out = []
+    for d in range(R):
+        lst = []
+        for e in range(d * epr, (d + 1) * epr):
+            for s in range(R):
+                for t in range(T):
+                    for j in range(k):
+                        if int(ids[s][t][j]) == e:
+                            lst.append((s, t, j, e))
+        out.append(lst)
+    return out

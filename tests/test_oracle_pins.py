@@ -454,3 +454,94 @@ def test_dropped_slots_add_nothing():
     assert out["pos"][0, 1, 0] == -1 and out["pos"][1, 4, 1] == -1
     assert np.array_equal(out["y"][0, 1], (np.float64(gates[0, 1, 1]) * x[0, 1]).astype(np.float32))
     assert np.array_equal(out["y"][1, 4], (np.float64(gates[1, 4, 0]) * x[1, 4]).astype(np.float32))
+
+
+# --------------------------------------------------------- expert-major receive layout
+
+def _check_expert_major_against_naive(ids, R, T, k, epr):
+    x = _tags(R, T, 3)
+    cap = R * T * k
+    d = oracle.dispatch(oracle.as_rows(x), ids, epr, cap, oracle.EXPERT_MAJOR)
+    rl = naive.recv_lists_expert_major(ids, R, T, k, epr)
+    recv = d["recv"].view(np.int32).reshape(R, cap, 3)
+    for dst in range(R):
+        assert d["recv_off"][dst, R] == len(rl[dst])
+        for q, (s, t, j, e) in enumerate(rl[dst]):
+            assert recv[dst, q, 0] == s and recv[dst, q, 1] == t
+        # group starts: rows of d's local expert le begin at recv_eoff[d][le]
+        for le in range(epr):
+            first = next((q for q, r in enumerate(rl[dst]) if r[3] == dst * epr + le), None)
+            if first is not None:
+                assert d["recv_eoff"][dst, le] == first
+        assert d["recv_eoff"][dst, epr] == len(rl[dst])
+
+
+@pytest.mark.parametrize("T,E,k", [(2, 2, 1), (2, 2, 2), (2, 4, 1), (2, 4, 2), (4, 4, 1)])
+def test_expert_major_bruteforce_every_id_pattern_two_ranks(T, E, k):
+    R, epr = 2, E // 2
+    for combo in itertools.product(range(E), repeat=R * T * k):
+        ids = np.array(combo, np.int32).reshape(R, T, k)
+        _check_expert_major_against_naive(ids, R, T, k, epr)
+
+
+@pytest.mark.parametrize("R,T,k,epr,seed", [(2, 50, 2, 2, 0), (4, 64, 2, 4, 1), (16, 12, 8, 16, 3), (5, 9, 5, 3, 5)])
+def test_expert_major_groups_and_tables(R, T, k, epr, seed):
+    rng = np.random.default_rng(seed)
+    E = R * epr
+    ids = _random_ids(rng, R, T, k, E)
+    cap = R * T * min(k, epr)
+    sm = oracle.dispatch(oracle.as_rows(_tags(R, T, 4)), ids, epr, cap, oracle.SOURCE_MAJOR)
+    em = oracle.dispatch(oracle.as_rows(_tags(R, T, 4)), ids, epr, cap, oracle.EXPERT_MAJOR)
+    # the layout does not change counts, offsets of the send side, or positions
+    for key in ("cnt", "send_off", "pos", "send", "recv_counts", "recv_off", "recv_eoff"):
+        assert np.array_equal(sm[key], em[key]), key
+    # group starts: exclusive prefix over local experts of the column sums of cnt
+    col = em["cnt"].sum(axis=0).reshape(R, epr)
+    assert np.array_equal(em["recv_eoff"], np.concatenate([np.zeros((R, 1), np.int64), np.cumsum(col, axis=1)], 1))
+    rs = sm["recv"].view(np.int32).reshape(R, cap, 4)
+    re_ = em["recv"].view(np.int32).reshape(R, cap, 4)
+    for dst in range(R):
+        n = em["recv_off"][dst, R]
+        # the same rows, another order
+        assert sorted(map(tuple, rs[dst, :n])) == sorted(map(tuple, re_[dst, :n]))
+        for le in range(epr):
+            lo, hi = em["recv_eoff"][dst, le], em["recv_eoff"][dst, le + 1]
+            rows = re_[dst, lo:hi]
+            e = dst * epr + le
+            # every row of the group chose expert e; sources ascend, tokens ascend per source
+            assert all(e in ids[s, t] for s, t in rows[:, :2])
+            key = rows[:, 0].astype(np.int64) * T + rows[:, 1]
+            assert np.all(np.diff(key) >= 0)
+
+
+@pytest.mark.parametrize("R,T,k,epr", [(2, 7, 1, 1), (4, 64, 2, 2), (16, 9, 8, 16), (3, 20, 3, 4)])
+def test_expert_major_return_inverts_the_exchange(R, T, k, epr):
+    rng = np.random.default_rng(R * T)
+    ids = _random_ids(rng, R, T, k, R * epr)
+    cap = R * T * min(k, epr)
+    d = oracle.dispatch(oracle.as_rows(_tags(R, T, 3)), ids, epr, cap, oracle.EXPERT_MAJOR)
+    ret = oracle.return_exchange(d["recv"], d["send_off"], d["recv_off"], T, k, d["cnt"], epr, oracle.EXPERT_MAJOR)
+    assert np.array_equal(ret, d["send"])
+
+
+def test_expert_major_capacity_overflow_drops_the_last_rows():
+    rng = np.random.default_rng(8)
+    R, T, k, epr = 4, 40, 2, 3
+    ids = _random_ids(rng, R, T, k, R * epr)
+    full = oracle.dispatch(oracle.as_rows(_tags(R, T, 3)), ids, epr, R * T * k, oracle.EXPERT_MAJOR)
+    cap = int(full["recv_off"][:, R].max()) - 4
+    d = oracle.dispatch(oracle.as_rows(_tags(R, T, 3)), ids, epr, cap, oracle.EXPERT_MAJOR)
+    assert d["status"] == oracle.ST_RECV_OVERFLOW
+    assert np.array_equal(d["recv"].view(np.int32).reshape(R, cap, 3),
+                          full["recv"].view(np.int32).reshape(R, -1, 3)[:, :cap])
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "wide", "edge"])
+def test_expert_major_staged_path_equals_closed_form(name):
+    small = dict(tiny={}, decode={}, wide=dict(tokens_per_rank=32, hidden=256), edge={})[name]
+    w = W.workload(name, **small)
+    x, ids, gates = W.make_inputs(w)
+    out = oracle.full_step(x, ids, gates, w.experts_per_rank, w.dtype, w.expert_mode, w.capacity, oracle.EXPERT_MAJOR)
+    y2 = oracle.closed_form(x, ids, gates, w.experts_per_rank, w.dtype, w.expert_mode)
+    assert out["status"] == 0
+    assert np.array_equal(out["y"], y2)
