@@ -80,8 +80,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode-graph", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
-    ap.add_argument("--paths", default="staged,direct",
-                    help="paths to time; the first one gives the headline value")
+    ap.add_argument("--paths", default="staged,direct,direct-expert-major",
+                    help="paths to time (staged, direct, staged-expert-major, direct-expert-major); "
+                         "the first one gives the headline value")
     ap.add_argument("--profile-summary", nargs="+", metavar="DB",
                     help="print per-kernel statistics of rocprofv3 database(s) and exit (no GPU)")
     args = ap.parse_args()
@@ -155,7 +156,7 @@ def main():
         "roofline": dict(head["roofline"], copy_reference_GBps=round(copy_gbps, 1)),
     }
     for p in paths[1:]:
-        result[f"{p}_path"] = {k: v for k, v in measured[p].items() if k != "ms_per_step_wall"}
+        result[f"{p.replace('-', '_')}_path"] = {k: v for k, v in measured[p].items() if k != "ms_per_step_wall"}
     del xt
     torch.cuda.empty_cache()
 
@@ -168,12 +169,21 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def time_path(torch, a2av, w, xt, idt, gt, path, steps, warmup):
+def path_config(a2av, name):
+    """'staged' | 'direct', optionally with '-expert-major': (path, receive layout)."""
+    path = a2av.PATH_DIRECT if name.startswith("direct") else a2av.PATH_STAGED
+    layout = a2av.LAYOUT_EXPERT_MAJOR if name.endswith("expert-major") else a2av.LAYOUT_SOURCE_MAJOR
+    return path, layout
+
+
+def time_path(torch, a2av, w, xt, idt, gt, name, steps, warmup):
     """Warm-up, then `steps` timed steps of one path with HIP events recorded between the
     library's kernels (on the stream they run on) and the wall clock around them."""
-    direct = path == "direct"
+    path_id, layout = path_config(a2av, name)
+    direct = path_id == a2av.PATH_DIRECT
+    path = name
     s = a2av.Session(w.num_ranks, w.tokens_per_rank, w.hidden, w.dtype, w.experts_per_rank, w.top_k,
-                     w.recv_capacity_rows, path=a2av.PATH_DIRECT if direct else a2av.PATH_STAGED)
+                     w.recv_capacity_rows, path=path_id, recv_layout=layout)
     y = torch.empty_like(xt)
 
     def step():
@@ -197,13 +207,15 @@ def time_path(torch, a2av, w, xt, idt, gt, path, steps, warmup):
     status = int(s.status.item())
     if status != 0:
         raise RuntimeError(f"device status {status} during the benchmark")
-    stage_ms = {n: ms_sum[i] / launches[i] for i, n in enumerate(a2av.STAGE_NAMES) if launches[i]}
+    # per step (a stage may launch more than one kernel), and per launch
+    stage_ms = {n: ms_sum[i] / steps for i, n in enumerate(a2av.STAGE_NAMES) if launches[i]}
+    launch_ms = {n: ms_sum[i] / launches[i] for i, n in enumerate(a2av.STAGE_NAMES) if launches[i]}
     dc_ms = sum(stage_ms.values())
     nbytes = step_bytes(w, direct)
     gbps = nbytes / (dc_ms * 1e-3) / 1e9
     sb = stage_bytes(w)
-    dom = max((n for n in stage_ms if n != "plan"), key=lambda n: stage_ms[n])
-    dom_gbps = sb[dom] / (stage_ms[dom] * 1e-3) / 1e9
+    dom = max((n for n in launch_ms if n != "plan"), key=lambda n: launch_ms[n])
+    dom_gbps = sb[dom] / (launch_ms[dom] * 1e-3) / 1e9
     log(f"{path}: stages (us/launch): " + ", ".join(f"{n} {v * 1e3:.1f}" for n, v in stage_ms.items()))
     s.close()
     del y, s
@@ -219,6 +231,7 @@ def time_path(torch, a2av, w, xt, idt, gt, path, steps, warmup):
             "bound": "hbm", "kernel": dom, "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
             "traffic": measured_traffic(w.name, path, dom), "bytes_per_launch": sb[dom],
+            "us_per_launch": round(launch_ms[dom] * 1e3, 2),
         },
     }
 
@@ -238,8 +251,9 @@ def decode_graph(np, torch, a2av, W, path, steps=100):
     ids = torch.empty((w.num_ranks, w.tokens_per_rank, w.top_k), dtype=torch.int32, device="cuda")
     gates = torch.empty((w.num_ranks, w.tokens_per_rank, w.top_k), dtype=torch.float32, device="cuda")
     y = torch.empty_like(xt)
+    path_id, layout = path_config(a2av, path)
     s = a2av.Session(w.num_ranks, w.tokens_per_rank, w.hidden, w.dtype, w.experts_per_rank, w.top_k,
-                     path=a2av.PATH_DIRECT if path == "direct" else a2av.PATH_STAGED)
+                     path=path_id, recv_layout=layout)
 
     def step():
         a2av.a2av_route_step(ids_table, gates_table, steps, n, counter, ids, gates)
@@ -270,7 +284,7 @@ def decode_graph(np, torch, a2av, W, path, steps=100):
     ok = int(counter.item()) == steps and int(s.status.item()) == 0
     out = {"workload": w.describe(), "replays": steps, "us_per_step_with_expert_and_router": round(us, 2),
            "host_syncs_between_replays": 0, "counter_ok": ok,
-           "algorithmic_bytes_per_step": step_bytes(w, path == "direct")}
+           "algorithmic_bytes_per_step": step_bytes(w, path_id == a2av.PATH_DIRECT)}
     s.close()
     del g
     torch.cuda.empty_cache()

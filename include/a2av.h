@@ -45,14 +45,20 @@
  *   x, y          [R][T][H]       dtype     token rows, one slice per rank
  *   topk_ids      [R][T][k]       int32     expert ids from the router
  *   gates         [R][T][k]       float32   combine weights
- *   recv, expert_out [R][cap][H]  dtype     receive rows; rank d's rows from source s
- *                                           are rows recv_offsets[d][s] ..
- *                                           recv_offsets[d][s+1]-1 of slice d, sorted
- *                                           by (expert, token, slot) as sent
+ *   recv, expert_out [R][cap][H]  dtype     receive rows.  Source-major layout: rank d's
+ *                                           rows from source s are rows recv_offsets[d][s]
+ *                                           .. recv_offsets[d][s+1]-1 of slice d, sorted
+ *                                           by (expert, token, slot) as sent.  Expert-major
+ *                                           layout: rows of d's local expert le are rows
+ *                                           recv_expert_offsets[d][le] .. [le+1]-1, source
+ *                                           ascending, each source in its sent order
+ *   recv_expert_offsets [R][epr+1] int32    expert-major group starts ([d][epr] = total)
  *   split         [R][E]          int32     rows rank s sends to expert e
  *   recv_counts   [R][R]          int32     [dst][src] rows received
  *   recv_offsets  [R][R+1]        int32     [dst][src] exclusive prefix over src;
- *                                           [dst][R] = rows rank dst received
+ *                                           [dst][R] = rows rank dst received (with the
+ *                                           expert-major layout these are counts, not
+ *                                           places)
  *   positions     [R][T][k]       int32     place of (t, slot) in rank s's expert-
  *                                           sorted send order, -1 if the id was invalid
  * Counts and offsets are in rows; byte addresses are formed in 64 bits.
@@ -87,6 +93,13 @@ typedef struct a2av_context* a2av_handle_t;
 #define A2AV_PATH_DIRECT 1        /* pack straight into the receivers' buffers; combine
                                      gathers the expert outputs where they are */
 
+/* receive layouts (a2av_config_t.recv_layout) */
+#define A2AV_LAYOUT_SOURCE_MAJOR 0  /* rows from source 0 first, each source's rows in its
+                                       sorted order (a plain all-to-allv) */
+#define A2AV_LAYOUT_EXPERT_MAJOR 1  /* rows grouped by the receiver's local expert, then by
+                                       source, then in the source's order: each expert's
+                                       rows contiguous, ready for a grouped expert GEMM */
+
 /* expert stand-ins of the harness call a2av_expert_apply */
 #define A2AV_EXPERT_IDENTITY 0    /* out = in */
 #define A2AV_EXPERT_SCALE    1    /* out = round(in * (1 + e/256)), e = the row's expert */
@@ -103,7 +116,7 @@ typedef struct {
                                    allocation size, never a transfer size. */
     int32_t path;               /* A2AV_PATH_STAGED or A2AV_PATH_DIRECT; both give the
                                    same receive rows, tables and combine results */
-    int32_t reserved;           /* must be 0 */
+    int32_t recv_layout;        /* A2AV_LAYOUT_SOURCE_MAJOR or A2AV_LAYOUT_EXPERT_MAJOR */
 } a2av_config_t;
 
 /* Validate cfg (host) and allocate the handle's device workspace on the current GPU:
@@ -156,7 +169,7 @@ int a2av_combine(a2av_handle_t h, const void* expert_out, const float* gates, vo
  * send_counts[s][0..d-1]; send_counts (device) [R][R] ([src][dst]) is read when the
  * kernels run, so it may be written by earlier work on the stream.  Rows land in recv
  * (device) [R][cap][H] source-major; recv_counts / recv_offsets (device, optional) as
- * for dispatch.  A negative count, or counts of one sender summing past T*k, set
+ * for dispatch (always source-major).  A negative count, or counts of one sender summing past T*k, set
  * A2AV_ST_EXPERT_RANGE and that sender's counts are taken as 0.  It replaces the
  * handle's routing state: a2av_combine and a2av_expert_apply after it return
  * A2AV_ERR_INVALID until the next a2av_dispatch.
@@ -166,6 +179,11 @@ int a2av_alltoallv(a2av_handle_t h, const void* send, const int32_t* send_counts
 
 /* Copy the position table of the latest dispatch into pos (device) [R][T][k]. */
 int a2av_copy_positions(a2av_handle_t h, int32_t* pos, void* stream);
+
+/* Copy where each local expert's rows start in the expert-major receive layout into
+ * recv_expert_offsets (device) [R][epr+1] ([d][epr] = rows d received).  Only for a
+ * handle created with A2AV_LAYOUT_EXPERT_MAJOR (else A2AV_ERR_INVALID). */
+int a2av_copy_recv_expert_offsets(a2av_handle_t h, int32_t* recv_expert_offsets, void* stream);
 
 /* Copy the send offsets of the latest dispatch into send_offsets (device) [R][R+1]:
  * [s][d] = first row of s's segment for d, [s][R] = rows s sent. */
@@ -195,7 +213,8 @@ int a2av_route_step(const int32_t* ids_table, const float* gates_table, int32_t 
  * the recorded events, writes per-stage sums of milliseconds into ms_sum (host)
  * [A2AV_STAGES] and the number of timed launches per stage into launches (host)
  * [A2AV_STAGES], and releases the events.  Stages: 0 plan (histogram + scans), 1 pack,
- * 2 exchange, 3 return exchange, 4 combine (the direct path has no 2 and 3).  Events
+ * 2 exchange, 3 return exchange, 4 combine (the direct path has no 2 and 3; the
+ * expert-major layout adds a second, small launch to stage 0).  Events
  * recorded between kernels add a little time to each step while timing is on. */
 #define A2AV_STAGES 5
 int a2av_timing_begin(a2av_handle_t h, int32_t max_calls);

@@ -22,12 +22,15 @@ EXPERT_IDENTITY = 0
 EXPERT_SCALE = 1
 PATH_STAGED = 0
 PATH_DIRECT = 1
+LAYOUT_SOURCE_MAJOR = 0
+LAYOUT_EXPERT_MAJOR = 1
 STAGES = 5
 STAGE_NAMES = ("plan", "pack", "exchange", "return", "combine")
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liba2av.so")
 EXPORTS = ("a2av_create", "a2av_destroy", "a2av_workspace_bytes", "a2av_dispatch", "a2av_combine",
-           "a2av_alltoallv", "a2av_copy_positions", "a2av_copy_send_offsets", "a2av_expert_apply",
+           "a2av_alltoallv", "a2av_copy_positions", "a2av_copy_recv_expert_offsets", "a2av_copy_send_offsets",
+           "a2av_expert_apply",
            "a2av_route_step", "a2av_timing_begin", "a2av_timing_end", "a2av_error_string")
 
 TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16}
@@ -37,7 +40,7 @@ class Config(ctypes.Structure):
     _fields_ = [("num_ranks", ctypes.c_int32), ("tokens_per_rank", ctypes.c_int32),
                 ("hidden", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("experts_per_rank", ctypes.c_int32), ("top_k", ctypes.c_int32),
-                ("recv_capacity_rows", ctypes.c_int64), ("path", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("recv_capacity_rows", ctypes.c_int64), ("path", ctypes.c_int32), ("recv_layout", ctypes.c_int32)]
 
 
 class A2AVError(RuntimeError):
@@ -67,6 +70,7 @@ def lib():
         L.a2av_alltoallv.argtypes = [vp] * 8
         L.a2av_copy_positions.argtypes = [vp, vp, vp]
         L.a2av_copy_send_offsets.argtypes = [vp, vp, vp]
+        L.a2av_copy_recv_expert_offsets.argtypes = [vp, vp, vp]
         L.a2av_expert_apply.argtypes = [vp, vp, vp, i32, vp]
         L.a2av_route_step.argtypes = [vp, vp, i32, i64, vp, vp, vp, vp]
         L.a2av_timing_begin.argtypes = [vp, i32]
@@ -108,8 +112,9 @@ def _check(fn, rc):
 
 
 def make_config(num_ranks, tokens_per_rank, hidden, dtype, experts_per_rank, top_k, recv_capacity_rows=0,
-                path=PATH_STAGED) -> Config:
-    return Config(num_ranks, tokens_per_rank, hidden, dtype, experts_per_rank, top_k, recv_capacity_rows, path, 0)
+                path=PATH_STAGED, recv_layout=LAYOUT_SOURCE_MAJOR) -> Config:
+    return Config(num_ranks, tokens_per_rank, hidden, dtype, experts_per_rank, top_k, recv_capacity_rows, path,
+                  recv_layout)
 
 
 def a2av_workspace_bytes(cfg: Config) -> int:
@@ -147,6 +152,11 @@ def a2av_copy_positions(h, pos, stream=None) -> None:
     _check("a2av_copy_positions", lib().a2av_copy_positions(h, _ptr(pos), _stream(stream)))
 
 
+def a2av_copy_recv_expert_offsets(h, recv_expert_offsets, stream=None) -> None:
+    _check("a2av_copy_recv_expert_offsets",
+           lib().a2av_copy_recv_expert_offsets(h, _ptr(recv_expert_offsets), _stream(stream)))
+
+
 def a2av_copy_send_offsets(h, send_offsets, stream=None) -> None:
     _check("a2av_copy_send_offsets", lib().a2av_copy_send_offsets(h, _ptr(send_offsets), _stream(stream)))
 
@@ -181,10 +191,12 @@ class Session:
     """
 
     def __init__(self, num_ranks, tokens_per_rank, hidden, dtype, experts_per_rank, top_k,
-                 recv_capacity_rows=0, path=PATH_STAGED, device="cuda"):
+                 recv_capacity_rows=0, path=PATH_STAGED, recv_layout=LAYOUT_SOURCE_MAJOR, device="cuda"):
         self.cfg = make_config(num_ranks, tokens_per_rank, hidden, dtype, experts_per_rank, top_k,
-                               recv_capacity_rows, path)
+                               recv_capacity_rows, path, recv_layout)
         self.path = path
+        self.recv_layout = recv_layout
+        self.epr = experts_per_rank
         self.R, self.T, self.H, self.k = num_ranks, tokens_per_rank, hidden, top_k
         self.E = num_ranks * experts_per_rank
         self.cap = recv_capacity_rows or num_ranks * tokens_per_rank * min(top_k, experts_per_rank)
@@ -217,6 +229,11 @@ class Session:
         pos = torch.empty((self.R, self.T, self.k), dtype=torch.int32, device=self.device)
         a2av_copy_positions(self.handle, pos)
         return pos
+
+    def recv_expert_offsets(self):
+        out = torch.empty((self.R, self.epr + 1), dtype=torch.int32, device=self.device)
+        a2av_copy_recv_expert_offsets(self.handle, out)
+        return out
 
     def send_offsets(self):
         so = torch.empty((self.R, self.R + 1), dtype=torch.int32, device=self.device)

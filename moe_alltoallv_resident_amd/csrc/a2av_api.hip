@@ -59,7 +59,7 @@ bool make_shape(const a2av_config_t* c, Shape* sh) {
     if (cap == 0) cap = (int64_t)c->num_ranks * c->tokens_per_rank * std::min<int64_t>(c->top_k, c->experts_per_rank);
     if (cap > INT32_MAX) return false;
     if (c->path != A2AV_PATH_STAGED && c->path != A2AV_PATH_DIRECT) return false;
-    if (c->reserved != 0) return false;
+    if (c->recv_layout != A2AV_LAYOUT_SOURCE_MAJOR && c->recv_layout != A2AV_LAYOUT_EXPERT_MAJOR) return false;
     sh->R = c->num_ranks;
     sh->T = c->tokens_per_rank;
     sh->k = c->top_k;
@@ -72,11 +72,12 @@ bool make_shape(const a2av_config_t* c, Shape* sh) {
     sh->cap = cap;
     sh->row_bytes = (int64_t)c->hidden * (c->dtype == A2AV_BF16 ? 2 : 4);
     sh->num_cu = 256;
+    sh->layout = c->recv_layout;
     return true;
 }
 
 struct MetaLayout {
-    size_t pos, cnt, send_off, recv_counts, recv_off, total;
+    size_t pos, cnt, send_off, recv_counts, recv_off, eoff, xbase, recv_eoff, total;
 };
 
 MetaLayout meta_layout(const Shape& sh) {
@@ -87,6 +88,9 @@ MetaLayout meta_layout(const Shape& sh) {
     m.send_off = o;    o += align_up(sizeof(int32_t) * (size_t)sh.R * (sh.R + 1));
     m.recv_counts = o; o += align_up(sizeof(int32_t) * (size_t)sh.R * sh.R);
     m.recv_off = o;    o += align_up(sizeof(int32_t) * (size_t)sh.R * (sh.R + 1));
+    m.eoff = o;        o += align_up(sizeof(int32_t) * (size_t)sh.R * (sh.E + 1));
+    m.xbase = o;       o += align_up(sizeof(int32_t) * (size_t)sh.R * sh.E);
+    m.recv_eoff = o;   o += align_up(sizeof(int32_t) * (size_t)sh.R * (sh.epr + 1));
     m.total = o;
     return m;
 }
@@ -181,6 +185,9 @@ int a2av_create(const a2av_config_t* cfg, a2av_handle_t* out) {
     h->tb.send_off = reinterpret_cast<int32_t*>(b + m.send_off);
     h->tb.recv_counts = reinterpret_cast<int32_t*>(b + m.recv_counts);
     h->tb.recv_off = reinterpret_cast<int32_t*>(b + m.recv_off);
+    h->tb.eoff = reinterpret_cast<int32_t*>(b + m.eoff);
+    h->tb.xbase = reinterpret_cast<int32_t*>(b + m.xbase);
+    h->tb.recv_eoff = reinterpret_cast<int32_t*>(b + m.recv_eoff);
     // tables start at zero
     if (hipMemset(h->meta, 0, m.total) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
         (void)hipFree(h->meta);
@@ -217,6 +224,10 @@ int a2av_dispatch(a2av_handle_t h, const void* x, const int32_t* topk_ids, void*
     const a2av::Tables& tb = h->tb;
     int rc = launch_timed(h, kStagePlan, st, [&] { return a2av::launch_plan(sh, tb, topk_ids, out, status, st); });
     if (rc != A2AV_OK) return rc;
+    if (sh.layout == A2AV_LAYOUT_EXPERT_MAJOR) {
+        rc = launch_timed(h, kStagePlan, st, [&] { return a2av::launch_layout(sh, tb, st); });
+        if (rc != A2AV_OK) return rc;
+    }
     void* dst = h->direct ? recv : h->send_buf;
     rc = launch_timed(h, kStagePack, st,
                       [&] { return a2av::launch_pack(sh, tb, out, status, x, dst, h->direct, vec, st); });
@@ -278,6 +289,14 @@ int a2av_copy_positions(a2av_handle_t h, int32_t* pos, void* stream) {
     if (!pos) return A2AV_ERR_INVALID;
     return hipMemcpyAsync(pos, h->tb.pos, n, hipMemcpyDeviceToDevice, static_cast<hipStream_t>(stream)) == hipSuccess
                ? A2AV_OK : A2AV_ERR_HIP;
+}
+
+int a2av_copy_recv_expert_offsets(a2av_handle_t h, int32_t* recv_expert_offsets, void* stream) {
+    if (!h || !recv_expert_offsets || !on_device(h)) return A2AV_ERR_INVALID;
+    if (h->sh.layout != A2AV_LAYOUT_EXPERT_MAJOR) return A2AV_ERR_INVALID;
+    const size_t n = sizeof(int32_t) * (size_t)h->sh.R * (h->sh.epr + 1);
+    return hipMemcpyAsync(recv_expert_offsets, h->tb.recv_eoff, n, hipMemcpyDeviceToDevice,
+                          static_cast<hipStream_t>(stream)) == hipSuccess ? A2AV_OK : A2AV_ERR_HIP;
 }
 
 int a2av_copy_send_offsets(a2av_handle_t h, int32_t* send_offsets, void* stream) {

@@ -20,6 +20,7 @@ struct Shape {
     int64_t cap;        // receive rows per rank
     int64_t row_bytes;  // H * element bytes
     int32_t num_cu;     // compute units of the device (sizes row splitting)
+    int32_t layout;     // 0 source-major receive buffers, 1 expert-major
 };
 
 // Device tables in the handle's workspace (rank-major, int32 rows).
@@ -29,6 +30,9 @@ struct Tables {
     int32_t* send_off;     // [R][R+1]  segment starts in each send buffer
     int32_t* recv_counts;  // [R][R]    [dst][src]
     int32_t* recv_off;     // [R][R+1]  [dst][src] exclusive prefix over src, [dst][R] total
+    int32_t* eoff;         // [R][E+1]  first place of each expert in the sender's order
+    int32_t* xbase;        // [R][E]    expert-major: receive place of (sender, expert)'s first row
+    int32_t* recv_eoff;    // [R][epr+1] expert-major: where each local expert's rows start
 };
 
 // Optional copies of the tables for the caller (any may be null).
@@ -47,6 +51,8 @@ int plan_waves(int32_t E);
 
 hipError_t launch_plan(const Shape& sh, const Tables& tb, const int32_t* ids, const Outputs& out,
                        uint32_t* status, hipStream_t st);
+// Expert-major receive places (one wavefront per receiver); after planning.
+hipError_t launch_layout(const Shape& sh, const Tables& tb, hipStream_t st);
 hipError_t launch_plan_from_counts(const Shape& sh, const Tables& tb, const int32_t* send_counts,
                                    uint32_t* status, hipStream_t st);
 // pack: staged (dst = send buffer) or direct (dst = receive buffer); also builds the

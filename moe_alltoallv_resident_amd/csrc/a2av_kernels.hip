@@ -246,6 +246,7 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanArgs a) {
     // send segments: destination d holds experts d*epr .. d*epr+epr-1, which are
     // consecutive in the sorted order
     for (int d = tid; d <= R; d += nt) a.tb.send_off[(int64_t)s * (R + 1) + d] = d < R ? tot[d * sh.epr] : total;
+    for (int e = tid; e <= E; e += nt) a.tb.eoff[(int64_t)s * (E + 1) + e] = e < E ? tot[e] : total;
     for (int i = tid; i < nw * E; i += nt) cw[i] += tot[i % E];
     __syncthreads();
 
@@ -262,6 +263,59 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanArgs a) {
             pos[i] = (e >= 0 && e < E) ? mine[e] + pos[i] : -1;
         }
     }
+}
+
+// Expert-major receive places.  Receiver d's rows are grouped by local expert, then by
+// sender, then in the sender's order.  One wavefront per receiver; lane l owns d's local
+// experts l, l+64, ...: it sums its expert's column of cnt over the senders (loads issued
+// together), a wavefront scan of those totals gives where each expert's group starts
+// (recv_eoff), and a second walk over the senders gives xbase[s][e], the place of the
+// first row s sends to e.
+__global__ void __launch_bounds__(kBlock) layout_kernel(Shape sh, Tables tb) {
+    const int lane = lane_id();
+    const int d = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
+    if (d >= sh.R) return;
+    const int R = sh.R, E = sh.E, epr = sh.epr;
+    int carry = 0;
+    for (int l0 = 0; l0 < epr; l0 += kWave) {
+        const int le = l0 + lane;
+        const bool mine = le < epr;
+        const int e = d * epr + le;
+        int total = 0;
+        if (mine)
+            for (int s = 0; s < R; ++s) total += tb.cnt[(int64_t)s * E + e];
+        const int incl = wave_inclusive_scan(total);
+        const int start = carry + incl - total;
+        if (mine) {
+            tb.recv_eoff[(int64_t)d * (epr + 1) + le] = start;
+            int run = start;
+            for (int s = 0; s < R; ++s) {
+                tb.xbase[(int64_t)s * E + e] = run;
+                run += tb.cnt[(int64_t)s * E + e];
+            }
+        }
+        carry += __shfl(incl, kWave - 1, kWave);
+    }
+    if (lane == 0) tb.recv_eoff[(int64_t)d * (epr + 1) + epr] = carry;
+}
+
+// The expert of send row p of sender s, given its destination d: the number of d's
+// experts whose block in the sender's order ends at or before p (one ballot per 64).
+__device__ __forceinline__ int expert_of(const Shape& sh, const Tables& tb, int64_t s, int64_t p, int d, int lane) {
+    const int32_t* eo = tb.eoff + s * (sh.E + 1) + (int64_t)d * sh.epr;
+    int le = 0;
+    for (int c0 = 0; c0 < sh.epr; c0 += kWave) {
+        const int i = c0 + lane;
+        le += __popcll(__ballot(i < sh.epr && (int64_t)eo[i + 1] <= p));
+    }
+    return d * sh.epr + le;
+}
+
+// Expert-major receive place of send row p (destination d) of sender s.
+__device__ __forceinline__ int64_t expert_major_place(const Shape& sh, const Tables& tb, int64_t s, int64_t p, int d,
+                                                      int lane) {
+    const int e = expert_of(sh, tb, s, p, d, lane);
+    return (int64_t)tb.xbase[s * sh.E + e] + (p - tb.eoff[s * (sh.E + 1) + e]);
 }
 
 // The bare collective's planning: send offsets from caller counts, one block per sender.
@@ -383,7 +437,8 @@ __global__ void __launch_bounds__(kBlock) pack_kernel(const V* __restrict__ x, V
             if constexpr (DIRECT) {
                 const int d = segment_of(so, R, pj, lane);
                 if (d >= R) continue;                   // not a sent row (tables always place it)
-                const int64_t q = recv_base(tb.send_off, R, d, (int)s, lane) + (pj - so[d]);
+                const int64_t q = sh.layout ? expert_major_place(sh, tb, s, pj, d, lane)
+                                            : recv_base(tb.send_off, R, d, (int)s, lane) + (pj - so[d]);
                 if (q < 0 || q >= sh.cap) continue;     // past the receiver's capacity (flagged)
                 row = dst + ((int64_t)d * sh.cap + q) * nvec;
             } else {
@@ -426,9 +481,10 @@ __global__ void __launch_bounds__(kBlock) exchange_kernel(const V* __restrict__ 
     const int32_t* so = tb.send_off + s * (R + 1);
     if (p >= so[R]) return;
     const int d = segment_of(so, R, p, lane);
-    const int64_t base = FIRST ? recv_base(tb.send_off, R, d, (int)s, lane)
-                               : (int64_t)tb.recv_off[(int64_t)d * (R + 1) + s];
-    const int64_t q = base + (p - so[d]);
+    int64_t q;
+    if (FIRST) q = recv_base(tb.send_off, R, d, (int)s, lane) + (p - so[d]);   // the bare collective
+    else if (sh.layout) q = expert_major_place(sh, tb, s, p, d, lane);
+    else q = (int64_t)tb.recv_off[(int64_t)d * (R + 1) + s] + (p - so[d]);
     const int64_t send_row = s * sh.TK + p, recv_row = (int64_t)d * sh.cap + q;
     const bool in_cap = q >= 0 && q < sh.cap;
     if (!REVERSE) {
@@ -525,7 +581,8 @@ __global__ void __launch_bounds__(kBlock) combine_kernel(const typename Vec<B>::
             if (pj < 0 || pj >= sh.TK) continue;
             const int d = segment_of(so, R, pj, lane);
             if (d >= R) continue;
-            const int64_t q = (int64_t)tb.recv_off[(int64_t)d * (R + 1) + s] + (pj - so[d]);
+            const int64_t q = sh.layout ? expert_major_place(sh, tb, s, pj, d, lane)
+                                        : (int64_t)tb.recv_off[(int64_t)d * (R + 1) + s] + (pj - so[d]);
             if (lane == j && q >= 0 && q < sh.cap) my_row = (int64_t)d * sh.cap + q;
         }
     } else {
@@ -583,33 +640,23 @@ __global__ void __launch_bounds__(kBlock) expert_kernel(const typename Vec<B>::T
     const int32_t* so = tb.send_off + s * (R + 1);
     if (p >= so[R]) return;
     const int d = segment_of(so, R, p, lane);
-    const int64_t i = p - so[d];
-    const int64_t q = (int64_t)tb.recv_off[(int64_t)d * (R + 1) + s] + i;
+    const int e = expert_of(sh, tb, s, p, d, lane);
+    const int64_t q = sh.layout ? (int64_t)tb.xbase[s * sh.E + e] + (p - tb.eoff[s * (sh.E + 1) + e])
+                                : (int64_t)tb.recv_off[(int64_t)d * (R + 1) + s] + (p - so[d]);
     if (q < 0 || q >= sh.cap) return;
     const int64_t row = (int64_t)d * sh.cap + q;
     if (mode == 0) {
         if (in != out) copy_row<V, U, false>(out + row * nvec, in + row * nvec, pc.v0, pc.v1, lane);
         return;
     }
-    // local expert: number of the sender's per-expert counts for d whose running
-    // sum is at or below i
-    const int32_t* c = tb.cnt + s * sh.E + (int64_t)d * sh.epr;
-    int le = 0, carry = 0;
-    for (int c0 = 0; c0 < sh.epr; c0 += kWave) {
-        const int idx = c0 + lane;
-        const int v = idx < sh.epr ? c[idx] : 0;
-        const int incl = carry + wave_inclusive_scan(v);
-        le += __popcll(__ballot(idx < sh.epr && (int64_t)incl <= i));
-        carry = __shfl(incl, kWave - 1, kWave);
-    }
-    const float scale = 1.0f + (float)(d * sh.epr + le) / 256.0f;
+    const float scale = 1.0f + (float)e / 256.0f;
     const V* src = in + row * nvec;
     V* dst = out + row * nvec;
     for (int v = pc.v0 + lane; v < pc.v1; v += kWave) {
         const V r = src[v];
         float f[NE];
 #pragma unroll
-        for (int e = 0; e < NE; ++e) f[e] = El::get(r, e) * scale;
+        for (int c = 0; c < NE; ++c) f[c] = El::get(r, c) * scale;
         dst[v] = El::pack(f);
     }
 }
@@ -709,6 +756,11 @@ hipError_t launch_plan(const Shape& sh, const Tables& tb, const int32_t* ids, co
     else if (slices <= 4) hipLaunchKernelGGL(plan_kernel<4>, dim3(sh.R), dim3(nw * kWave), lds, st, a);
     else if (slices <= 8) hipLaunchKernelGGL(plan_kernel<8>, dim3(sh.R), dim3(nw * kWave), lds, st, a);
     else hipLaunchKernelGGL(plan_kernel<16>, dim3(sh.R), dim3(nw * kWave), lds, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_layout(const Shape& sh, const Tables& tb, hipStream_t st) {
+    hipLaunchKernelGGL(layout_kernel, dim3((unsigned)table_blocks(sh.R)), dim3(kBlock), 0, st, sh, tb);
     return hipGetLastError();
 }
 

@@ -76,11 +76,14 @@ class Run:
     """One dispatch -> expert stand-in -> combine pass of the HIP path, step by step,
     with the tables and rows copied to the host for comparison."""
 
-    def __init__(self, w: W.Workload, x, ids, gates, session=None, path=a2av.PATH_STAGED, device_inputs=None):
+    def __init__(self, w: W.Workload, x, ids, gates, session=None, path=a2av.PATH_STAGED,
+                 layout=a2av.LAYOUT_SOURCE_MAJOR, device_inputs=None):
         self.w = w
         self.x_dev, self.ids_dev, self.gates_dev = device_inputs or to_device(w, x, ids, gates)
         self.session = session or a2av.Session(w.num_ranks, w.tokens_per_rank, w.hidden, w.dtype,
-                                               w.experts_per_rank, w.top_k, w.recv_capacity_rows, path=path)
+                                               w.experts_per_rank, w.top_k, w.recv_capacity_rows, path=path,
+                                               recv_layout=layout)
+        self.layout = self.session.recv_layout
         self.recv = self.z = None
 
     def dispatch(self, keep_recv=True):
@@ -92,6 +95,7 @@ class Run:
         self.recv_off = host_bits(s.recv_offsets)
         self.pos = host_bits(s.positions())
         self.send_off = host_bits(s.send_offsets())
+        self.recv_eoff = host_bits(s.recv_expert_offsets()) if self.layout == a2av.LAYOUT_EXPERT_MAJOR else None
         self.valid = [int(min(self.recv_off[d, R], s.cap)) for d in range(R)]
         if keep_recv:
             self.recv = [host_bits(s.recv[d, :self.valid[d]]) for d in range(R)]
@@ -118,12 +122,12 @@ class Run:
         return self.dispatch(keep).expert(keep).combine()
 
 
-def oracle_tables(w: W.Workload, ids):
+def oracle_tables(w: W.Workload, ids, layout=oracle.SOURCE_MAJOR):
     """The oracle's dispatch with 4-byte tag rows (global token index): the full routing
     at any size, cheap because no hidden-size rows are moved."""
     R, T = w.num_ranks, w.tokens_per_rank
     tags = np.arange(R * T, dtype=np.int32).reshape(R, T, 1)
-    d = oracle.dispatch(oracle.as_rows(tags), ids, w.experts_per_rank, w.capacity)
+    d = oracle.dispatch(oracle.as_rows(tags), ids, w.experts_per_rank, w.capacity, layout)
     d["recv_tags"] = d["recv"].view(np.int32).reshape(R, w.capacity)
     return d
 
@@ -134,3 +138,5 @@ def assert_tables_equal(run: Run, ref: dict, R: int):
     assert np.array_equal(run.recv_counts, ref["recv_counts"]), "receive counts"
     assert np.array_equal(run.recv_off, ref["recv_off"]), "receive offsets"
     assert np.array_equal(run.pos, ref["pos"]), "positions"
+    if run.recv_eoff is not None:
+        assert np.array_equal(run.recv_eoff, ref["recv_eoff"]), "expert group starts"

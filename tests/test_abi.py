@@ -41,7 +41,7 @@ def test_error_strings():
 @pytest.mark.parametrize("bad", [
     dict(num_ranks=0), dict(num_ranks=2000), dict(tokens_per_rank=-1), dict(hidden=0), dict(dtype=7),
     dict(experts_per_rank=0), dict(experts_per_rank=513), dict(top_k=0), dict(top_k=65),
-    dict(num_ranks=2, experts_per_rank=1, top_k=3), dict(recv_capacity_rows=-5), dict(path=2),
+    dict(num_ranks=2, experts_per_rank=1, top_k=3), dict(recv_capacity_rows=-5), dict(path=2), dict(recv_layout=2),
 ])
 def test_workspace_bytes_rejects_invalid_configs(bad):
     base = dict(num_ranks=8, tokens_per_rank=128, hidden=5120, dtype=a2av.BF16, experts_per_rank=16, top_k=1)

@@ -16,9 +16,9 @@ from tests.gpu_util import assert_combine_close, banner, host_bits, to_device
 pytestmark = pytest.mark.gpu
 
 
-def _cfg(w, path=a2av.PATH_STAGED):
+def _cfg(w, path=a2av.PATH_STAGED, layout=a2av.LAYOUT_SOURCE_MAJOR):
     return a2av.make_config(w.num_ranks, w.tokens_per_rank, w.hidden, w.dtype, w.experts_per_rank, w.top_k,
-                            w.recv_capacity_rows, path)
+                            w.recv_capacity_rows, path, layout)
 
 
 def test_host_side_rejections_enqueue_nothing():
@@ -49,17 +49,22 @@ def test_host_side_rejections_enqueue_nothing():
     assert L.a2av_expert_apply(h, P(recv), P(recv), 7, stream) == a2av.ERR_INVALID
     torch.cuda.synchronize()
     assert int(st.item()) == 0
+    # the expert-major group starts exist only for that layout
+    with pytest.raises(a2av.A2AVError):
+        a2av.a2av_copy_recv_expert_offsets(h, torch.empty((w.num_ranks, w.experts_per_rank + 1), dtype=torch.int32,
+                                                          device="cuda"))
     a2av.a2av_destroy(h)
     # invalid configurations
-    for field, value in (("top_k", 99), ("path", 5), ("reserved", 1)):
+    for field, value in (("top_k", 99), ("path", 5), ("recv_layout", 3)):
         bad = _cfg(w)
         setattr(bad, field, value)
         with pytest.raises(a2av.A2AVError):
             a2av.a2av_create(bad)
 
 
+@pytest.mark.parametrize("layout", [a2av.LAYOUT_SOURCE_MAJOR, a2av.LAYOUT_EXPERT_MAJOR], ids=["srcmaj", "expmaj"])
 @pytest.mark.parametrize("path", [a2av.PATH_STAGED, a2av.PATH_DIRECT], ids=["staged", "direct"])
-def test_receive_overflow_keeps_guard_rows_and_true_counts(path):
+def test_receive_overflow_keeps_guard_rows_and_true_counts(path, layout):
     w = W.workload("wide", num_ranks=4, tokens_per_rank=64, hidden=96, experts_per_rank=2, top_k=2)
     x, ids, gates = W.make_inputs(w)
     full = oracle.dispatch(oracle.as_rows(x), ids, w.experts_per_rank, w.capacity)
@@ -76,11 +81,11 @@ def test_receive_overflow_keeps_guard_rows_and_true_counts(path):
     rc = torch.empty((R, R), dtype=torch.int32, device="cuda")
     ro = torch.empty((R, R + 1), dtype=torch.int32, device="cuda")
     st = torch.zeros(1, dtype=torch.int32, device="cuda")
-    h = a2av.a2av_create(_cfg(w, path))
+    h = a2av.a2av_create(_cfg(w, path, layout))
     a2av.a2av_dispatch(h, xt, idt, recv, split, rc, ro, st)
     torch.cuda.synchronize()
     assert int(st.item()) == a2av.ST_RECV_OVERFLOW
-    ref = oracle.dispatch(oracle.as_rows(x), ids, w.experts_per_rank, cap)
+    ref = oracle.dispatch(oracle.as_rows(x), ids, w.experts_per_rank, cap, layout)
     assert ref["status"] == oracle.ST_RECV_OVERFLOW
     assert np.array_equal(host_bits(rc), ref["recv_counts"])
     assert np.array_equal(host_bits(ro), ref["recv_off"])
@@ -97,7 +102,7 @@ def test_receive_overflow_keeps_guard_rows_and_true_counts(path):
     a2av.a2av_expert_apply(h, recv, recv, a2av.EXPERT_SCALE)
     a2av.a2av_combine(h, recv, gt, y, st)
     torch.cuda.synchronize()
-    oref = oracle.full_step(x, ids, gates, w.experts_per_rank, w.dtype, w.expert_mode, cap)
+    oref = oracle.full_step(x, ids, gates, w.experts_per_rank, w.dtype, w.expert_mode, cap, layout)
     assert_combine_close(host_bits(y), oref["y"], w.dtype, "overflow combine")
     a2av.a2av_destroy(h)
 

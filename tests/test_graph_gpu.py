@@ -29,11 +29,12 @@ def _tables(w, steps):
     return ids, gates
 
 
-@pytest.mark.parametrize("path", [a2av.PATH_STAGED, a2av.PATH_DIRECT], ids=["staged", "direct"])
+@pytest.mark.parametrize("path,layout", [(a2av.PATH_STAGED, 0), (a2av.PATH_DIRECT, 0), (a2av.PATH_DIRECT, 1)],
+                         ids=["staged", "direct", "direct-expmaj"])
 @pytest.mark.parametrize("name,steps,full_every", [("decode", 100, 10), ("edge", 24, 1)])
-def test_graph_replay_with_device_side_routing(name, steps, full_every, path):
+def test_graph_replay_with_device_side_routing(name, steps, full_every, path, layout):
     w = W.workload(name)
-    banner(f"graph replay {w.describe()} steps={steps} path={path}")
+    banner(f"graph replay {w.describe()} steps={steps} path={path} layout={layout}")
     x = W.make_x(w)
     ids_tab, gates_tab = _tables(w, steps)
     xt, _, _ = to_device(w, x, ids_tab[0], gates_tab[0])
@@ -44,7 +45,8 @@ def test_graph_replay_with_device_side_routing(name, steps, full_every, path):
     ids = torch.empty((w.num_ranks, w.tokens_per_rank, w.top_k), dtype=torch.int32, device="cuda")
     gates = torch.empty((w.num_ranks, w.tokens_per_rank, w.top_k), dtype=torch.float32, device="cuda")
     y = torch.empty_like(xt)
-    s = a2av.Session(w.num_ranks, w.tokens_per_rank, w.hidden, w.dtype, w.experts_per_rank, w.top_k, path=path)
+    s = a2av.Session(w.num_ranks, w.tokens_per_rank, w.hidden, w.dtype, w.experts_per_rank, w.top_k, path=path,
+                     recv_layout=layout)
 
     def step():
         a2av.a2av_route_step(ids_table, gates_table, steps, n, counter, ids, gates)

@@ -29,12 +29,14 @@ def _free():
 
 PATHS = [a2av.PATH_STAGED, a2av.PATH_DIRECT]
 PATH_IDS = ["staged", "direct"]
+LAYOUTS = [a2av.LAYOUT_SOURCE_MAJOR, a2av.LAYOUT_EXPERT_MAJOR]
+LAYOUT_IDS = ["srcmaj", "expmaj"]
 
 
-def _full_oracle_check(w: W.Workload, x, ids, gates, path=a2av.PATH_STAGED):
-    banner(f"full check {w.describe()} cap={w.capacity} path={PATH_IDS[path]}")
-    ref = oracle.full_step(x, ids, gates, w.experts_per_rank, w.dtype, w.expert_mode, w.capacity)
-    run = Run(w, x, ids, gates, path=path).all()
+def _full_oracle_check(w: W.Workload, x, ids, gates, path=a2av.PATH_STAGED, layout=a2av.LAYOUT_SOURCE_MAJOR):
+    banner(f"full check {w.describe()} cap={w.capacity} path={PATH_IDS[path]} layout={LAYOUT_IDS[layout]}")
+    ref = oracle.full_step(x, ids, gates, w.experts_per_rank, w.dtype, w.expert_mode, w.capacity, layout)
+    run = Run(w, x, ids, gates, path=path, layout=layout).all()
     R = w.num_ranks
     assert_tables_equal(run, ref, R)
     assert run.status == ref["status"], (run.status, ref["status"])
@@ -91,12 +93,13 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("layout", LAYOUTS, ids=LAYOUT_IDS)
 @pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
 @pytest.mark.parametrize("name,over", SMALL, ids=[f"{n}-{i}" for i, (n, _) in enumerate(SMALL)])
-def test_small_and_ragged_cases_match_oracle(name, over, path):
+def test_small_and_ragged_cases_match_oracle(name, over, path, layout):
     w = W.workload(name, **over)
     x, ids, gates = W.make_inputs(w)
-    ref = _full_oracle_check(w, x, ids, gates, path)
+    ref = _full_oracle_check(w, x, ids, gates, path, layout)
     if over.get("recv_capacity_rows"):
         assert ref["status"] & oracle.ST_RECV_OVERFLOW
 
@@ -115,12 +118,13 @@ def _random_case(i):
                       int(rng.integers(0, 2)), zipf_s=1.2, seed=i)
 
 
+@pytest.mark.parametrize("layout", LAYOUTS, ids=LAYOUT_IDS)
 @pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
 @pytest.mark.parametrize("i", range(12))
-def test_seeded_random_shapes_match_oracle(i, path):
+def test_seeded_random_shapes_match_oracle(i, path, layout):
     w = _random_case(i)
     x, ids, gates = W.make_inputs(w)
-    _full_oracle_check(w, x, ids, gates, path)
+    _full_oracle_check(w, x, ids, gates, path, layout)
 
 
 @pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
@@ -187,7 +191,7 @@ def test_full_size_workload(name):
     w = W.workload(name)
     banner(f"full size {w.describe()} cap={w.capacity}")
     x, ids, gates = W.make_inputs(w)
-    ref = oracle_tables(w, ids)
+    refs = {lay: oracle_tables(w, ids, lay) for lay in LAYOUTS}
     rng = np.random.default_rng(17)
     budget = {"prefill": 4096, "wide": 1024}.get(name, w.tokens)
     span = min(budget, 256) if budget < w.tokens else w.tokens
@@ -197,9 +201,10 @@ def test_full_size_workload(name):
              for a in starts}
     dev = to_device(w, x, ids, gates)
     yt = None
-    for path, pname in zip(PATHS, PATH_IDS):
-        banner(f"  path {pname}")
-        run = Run(w, x, ids, gates, path=path, device_inputs=dev).dispatch(keep_recv=False)
+    for path, pname, layout in [(p, n, lay) for p, n in zip(PATHS, PATH_IDS) for lay in LAYOUTS]:
+        banner(f"  path {pname} layout {LAYOUT_IDS[layout]}")
+        ref = refs[layout]
+        run = Run(w, x, ids, gates, path=path, layout=layout, device_inputs=dev).dispatch(keep_recv=False)
         assert_tables_equal(run, ref, w.num_ranks)
         assert run.session.status.item() == 0
 
