@@ -116,19 +116,26 @@ def main():
     measured = {p: time_path(torch, a2av, w, xt, idt, gt, p, args.steps, args.warmup) for p in paths}
     head = measured[paths[0]]
 
-    # achievable reference: a plain device copy of one stage's bytes (read + write)
+    # achievable references for one stage's bytes (read + write): torch's device copy and
+    # the library's reference row copy (the path's own row movement, identity mapping)
     ref_elems = w.assignments * w.row_bytes // 2
     src = torch.empty(ref_elems, dtype=torch.int16, device="cuda")
     dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(10):
-        dst.copy_(src)
-    e1.record()
-    torch.cuda.synchronize()
-    copy_gbps = 2 * ref_elems * 2 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+    def timed(fn, n=10):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    copy_gbps = 2 * ref_elems * 2 / (timed(lambda: dst.copy_(src)) * 1e-3) / 1e9
+    row_copy_gbps = 2 * ref_elems * 2 / (timed(lambda: a2av.a2av_copy_reference(src, dst, w.assignments, w.row_bytes))
+                                         * 1e-3) / 1e9
     del src, dst
 
     result = {
@@ -153,7 +160,9 @@ def main():
             "algorithmic_bytes_per_step": head["bytes_per_step"],
         },
         "stage_us": head["stage_us"],
-        "roofline": dict(head["roofline"], copy_reference_GBps=round(copy_gbps, 1)),
+        "roofline": dict(head["roofline"], copy_reference_GBps=round(copy_gbps, 1),
+                         row_copy_reference_GBps=round(row_copy_gbps, 1),
+                         frac_of_row_copy=round(head["roofline"]["achieved"] / row_copy_gbps, 4)),
     }
     for p in paths[1:]:
         result[f"{p.replace('-', '_')}_path"] = {k: v for k, v in measured[p].items() if k != "ms_per_step_wall"}

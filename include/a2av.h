@@ -206,6 +206,13 @@ int a2av_route_step(const int32_t* ids_table, const float* gates_table, int32_t 
 
 /* ---- measurement ----------------------------------------------------------------- */
 
+/* Reference row copy: dst[r] = src[r] for rows rows of row_bytes bytes (a multiple of
+ * 16; src, dst 16-byte aligned device pointers), moved exactly as the path's kernels move
+ * rows (16-byte vectors, one wavefront per row or per chunk, non-temporal when large).
+ * It measures the achievable copy bandwidth that the path's kernels are compared with.
+ * Errors: A2AV_ERR_INVALID, A2AV_ERR_HIP. */
+int a2av_copy_reference(const void* src, void* dst, int64_t rows, int64_t row_bytes, void* stream);
+
 /* Stage timing with HIP events recorded between the library's kernels on the call's
  * stream.  a2av_timing_begin(h, max_calls) creates events for up to max_calls
  * dispatch and max_calls combine calls (host-side event objects only; no device

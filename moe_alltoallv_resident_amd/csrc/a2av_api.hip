@@ -325,6 +325,17 @@ int a2av_route_step(const int32_t* ids_table, const float* gates_table, int32_t 
                                    static_cast<hipStream_t>(stream)) == hipSuccess ? A2AV_OK : A2AV_ERR_HIP;
 }
 
+int a2av_copy_reference(const void* src, void* dst, int64_t rows, int64_t row_bytes, void* stream) {
+    if (rows < 0 || row_bytes < 16 || row_bytes % 16 != 0) return A2AV_ERR_INVALID;
+    if (rows > 0 && (!src || !dst || ((uintptr_t)src % 16) != 0 || ((uintptr_t)dst % 16) != 0)) return A2AV_ERR_INVALID;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return A2AV_ERR_HIP;
+    return a2av::launch_reference_copy(src, dst, rows, row_bytes, cus, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? A2AV_OK : A2AV_ERR_HIP;
+}
+
 int a2av_timing_begin(a2av_handle_t h, int32_t max_calls) {
     if (!h || max_calls < 1) return A2AV_ERR_INVALID;
     drop_timing(h);

@@ -68,6 +68,8 @@ hipError_t launch_combine(const Shape& sh, const Tables& tb, const void* rows, c
                           bool direct, int vec, hipStream_t st);
 hipError_t launch_expert(const Shape& sh, const Tables& tb, const void* in, void* out, int mode, int vec,
                          hipStream_t st);
+hipError_t launch_reference_copy(const void* src, void* dst, int64_t rows, int64_t row_bytes, int num_cu,
+                                 hipStream_t st);
 hipError_t launch_route_step(const int32_t* ids_table, const float* gates_table, int32_t steps, int64_t n,
                              int32_t* counter, int32_t* ids, float* gates, hipStream_t st);
 

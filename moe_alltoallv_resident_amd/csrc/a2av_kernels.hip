@@ -661,6 +661,16 @@ __global__ void __launch_bounds__(kBlock) expert_kernel(const typename Vec<B>::T
     }
 }
 
+// Reference row copy (measurement harness): the same row movement as the exchange with
+// the identity mapping, for the achievable-bandwidth line next to the path's kernels.
+template <int U, bool NT>
+__global__ void __launch_bounds__(kBlock) reference_copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                                int64_t rows, Split sp) {
+    const Piece pc = piece_of((int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kWave, sp);
+    if (pc.row >= rows) return;
+    copy_row<u32x4, U, NT>(dst + pc.row * sp.nvec, src + pc.row * sp.nvec, pc.v0, pc.v1, lane_id());
+}
+
 __global__ void __launch_bounds__(1024) route_step_kernel(const int32_t* __restrict__ ids_table,
                                                           const float* __restrict__ gates_table, int32_t steps,
                                                           int64_t n, int32_t* counter, int32_t* __restrict__ ids,
@@ -746,7 +756,9 @@ int plan_waves(int32_t E) { return std::max(1, std::min(16, (int)(kPlanLdsBytes 
 
 hipError_t launch_plan(const Shape& sh, const Tables& tb, const int32_t* ids, const Outputs& out, uint32_t* status,
                        hipStream_t st) {
-    const int nw = plan_waves(sh.E);
+    // no more wavefronts than there are 64-assignment slices: idle ones would only add
+    // barrier and scan work
+    const int nw = (int)std::max<int64_t>(1, std::min<int64_t>(plan_waves(sh.E), (sh.TK + kWave - 1) / kWave));
     const size_t lds = (size_t)(nw + 1) * sh.E * sizeof(int);
     PlanArgs a{sh, tb, out, ids, status};
     const int64_t per_wave = (sh.TK + nw - 1) / nw;
@@ -894,6 +906,20 @@ hipError_t launch_expert(const Shape& sh, const Tables& tb, const void* in, void
         case 8: return launch_expert_t<8, 0>(sh, tb, in, out, mode, st);
         default: return launch_expert_t<4, 0>(sh, tb, in, out, mode, st);
     }
+}
+
+hipError_t launch_reference_copy(const void* src, void* dst, int64_t rows, int64_t row_bytes, int num_cu,
+                                 hipStream_t st) {
+    if (rows == 0) return hipSuccess;
+    const Split sp = make_split(row_bytes, 16, rows, num_cu);
+    return with_unroll(sp.cv, [&](auto U) {
+        return with_nt(rows * row_bytes, [&](auto NT) {
+            hipLaunchKernelGGL((reference_copy_kernel<decltype(U)::value, decltype(NT)::value>),
+                               dim3(piece_blocks(rows, sp)), dim3(kBlock), 0, st, (const u32x4*)src, (u32x4*)dst, rows,
+                               sp);
+            return hipGetLastError();
+        });
+    });
 }
 
 hipError_t launch_route_step(const int32_t* ids_table, const float* gates_table, int32_t steps, int64_t n,

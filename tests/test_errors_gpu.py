@@ -167,3 +167,18 @@ def test_zero_tokens(path):
     torch.cuda.synchronize()
     assert not split.any() and not rc.any() and not ro.any() and int(st.item()) == 0
     a2av.a2av_destroy(h)
+
+
+@pytest.mark.parametrize("rows,row_bytes", [(0, 16), (1, 16), (37, 10240), (1000, 4096), (65, 1040)])
+def test_reference_copy(rows, row_bytes):
+    src = torch.randint(-2 ** 15, 2 ** 15, (rows, row_bytes // 2), dtype=torch.int16, device="cuda")
+    dst = torch.zeros_like(src)
+    a2av.a2av_copy_reference(src, dst, rows, row_bytes)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
+    L = a2av.lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if rows:
+        assert L.a2av_copy_reference(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr() + 8), rows,
+                                     row_bytes, stream) == a2av.ERR_INVALID
+    assert L.a2av_copy_reference(None, None, 1, 24, stream) == a2av.ERR_INVALID
