@@ -110,10 +110,16 @@ int min_vec(const Shape& sh) { return sh.dtype == A2AV_F32 ? 4 : 2; }
 // Row arrays are empty when there are no tokens; their pointers may then be null.
 bool has_tokens(const Shape& sh) { return sh.T > 0; }
 
-// Launch one kernel, with timing events around it while timing slots remain.
+// Launch one kernel, with timing events around it while timing slots remain (never on a
+// stream that is being captured into a graph: the events belong to eager timing only).
 template <typename F>
 int launch_timed(a2av_context* h, int stage, hipStream_t st, F&& launch) {
-    TimedLaunch* t = h->timed_used < h->timed.size() ? &h->timed[h->timed_used++] : nullptr;
+    TimedLaunch* t = nullptr;
+    if (h->timed_used < h->timed.size()) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(st, &cs) != hipSuccess) return A2AV_ERR_HIP;
+        if (cs == hipStreamCaptureStatusNone) t = &h->timed[h->timed_used++];
+    }
     if (t) {
         t->stage = stage;
         if (hipEventRecord(t->a, st) != hipSuccess) return A2AV_ERR_HIP;

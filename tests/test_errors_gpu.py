@@ -182,3 +182,75 @@ def test_reference_copy(rows, row_bytes):
         assert L.a2av_copy_reference(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr() + 8), rows,
                                      row_bytes, stream) == a2av.ERR_INVALID
     assert L.a2av_copy_reference(None, None, 1, 24, stream) == a2av.ERR_INVALID
+
+
+def test_bare_alltoallv_reads_counts_by_reference():
+    """The counts are device data read when the collective executes: counts written by
+    GPU work enqueued just before the call (no host synchronisation in between) are the
+    ones used, eagerly and in a replayed graph whose captured producer changes them."""
+    R, T, H = 4, 32, 64
+    w = W.Workload("byref", R, T, H, W.BF16, 1, 1, "uniform", "softmax", 0)
+    x = W.make_x(w)
+    xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    h = a2av.a2av_create(_cfg(w))
+    recv = torch.empty((R, w.capacity, H), dtype=torch.bfloat16, device="cuda")
+    rc = torch.empty((R, R), dtype=torch.int32, device="cuda")
+    ro = torch.empty((R, R + 1), dtype=torch.int32, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    rng = np.random.default_rng(2)
+    tables = []
+    for _ in range(6):
+        dest = np.sort(rng.integers(0, R, size=(R, T)), axis=1)
+        tables.append(np.stack([np.bincount(dest[s], minlength=R) for s in range(R)]).astype(np.int32))
+    table_dev = torch.from_numpy(np.stack(tables)).cuda()
+    counts = torch.zeros((R, R), dtype=torch.int32, device="cuda")
+    step = torch.zeros(1, dtype=torch.int64, device="cuda")
+
+    def produce_and_exchange():
+        # a device-side producer picks this step's counts; nothing goes through the host
+        counts.copy_(table_dev.index_select(0, step).reshape(R, R))
+        step.add_(1)
+        a2av.a2av_alltoallv(h, xt, counts, recv, rc, ro, st)
+
+    def expect(i):
+        return oracle.dispatch(oracle.as_rows(x), _dest_ids(tables[i], T), 1, w.capacity)
+
+    produce_and_exchange()                               # eager, step 0
+    torch.cuda.synchronize()
+    ref = expect(0)
+    assert np.array_equal(host_bits(rc), ref["recv_counts"])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        produce_and_exchange()                           # step 1 (warm-up on the side stream)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        produce_and_exchange()
+    for i in range(2, 6):
+        step.fill_(i)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = expect(i)
+        assert np.array_equal(host_bits(rc), ref["recv_counts"]), f"replay for step {i}"
+        assert np.array_equal(host_bits(ro), ref["recv_off"])
+        got = host_bits(recv)
+        want = ref["recv"].view(np.uint16).reshape(R, w.capacity, H)
+        for d in range(R):
+            n = int(ref["recv_off"][d, R])
+            assert np.array_equal(got[d, :n], want[d, :n])
+    assert int(st.item()) == 0
+    del g
+    a2av.a2av_destroy(h)
+
+
+def _dest_ids(counts, T):
+    """Expert ids (one expert per rank, k = 1) whose expert-sorted order is the identity
+    and whose per-destination counts are `counts` [src][dst]."""
+    R = counts.shape[0]
+    ids = np.zeros((R, T, 1), np.int32)
+    for s in range(R):
+        ids[s, :, 0] = np.repeat(np.arange(R), counts[s])
+    return ids
