@@ -31,17 +31,25 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def kernel_source_sha256():
+    """Hash of the kernels' source (kernels and the shared layout header)."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in ("a2av_kernels.hip", "a2av_internal.h"):
+        with open(os.path.join(ROOT, "moe_alltoallv_resident_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def measured_traffic(workload, path, kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter passes
     (profiles/hbm_traffic.json: FETCH_SIZE and WRITE_SIZE scaled by a copy kernel of
     known size), or None when the kernels' source changed since the counters were taken
     or no counters exist for this workload and kernel."""
-    import hashlib
     try:
         with open(os.path.join(ROOT, "profiles", "hbm_traffic.json")) as f:
             rec = json.load(f)
-        with open(os.path.join(ROOT, "moe_alltoallv_resident_amd", "csrc", "a2av_kernels.hip"), "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
+        sha = kernel_source_sha256()
     except (OSError, ValueError):
         return None
     if rec.get("kernel_source_sha256") != sha or rec.get("workload") != workload:
@@ -270,30 +278,47 @@ def decode_graph(np, torch, a2av, W, path, steps=100):
         s.expert(s.recv, s.recv, w.expert_mode)
         s.combine(s.recv, gates, y)
 
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        step()
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        step()
-    for _ in range(10):
-        g.replay()
-    torch.cuda.synchronize()
+    def harness_only():
+        # the router and expert stand-ins alone (the expert reuses the last routing)
+        a2av.a2av_route_step(ids_table, gates_table, steps, n, counter, ids, gates)
+        s.expert(s.recv, s.recv, w.expert_mode)
+
+    def capture(fn):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            fn()
+        for _ in range(10):
+            graph.replay()
+        torch.cuda.synchronize()
+        return graph
+
+    def replay_us(graph):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / steps
+
+    g = capture(step)
+    gh = capture(harness_only)
     counter.zero_()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / steps
+    us = replay_us(g)
     ok = int(counter.item()) == steps and int(s.status.item()) == 0
+    us_h = replay_us(gh)
     out = {"workload": w.describe(), "replays": steps, "us_per_step_with_expert_and_router": round(us, 2),
+           "us_router_and_expert_only": round(us_h, 2),
+           "us_dispatch_combine_estimate": round(us - us_h, 2),
            "host_syncs_between_replays": 0, "counter_ok": ok,
            "algorithmic_bytes_per_step": step_bytes(w, path_id == a2av.PATH_DIRECT)}
+    del gh
     s.close()
     del g
     torch.cuda.empty_cache()
