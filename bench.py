@@ -87,7 +87,7 @@ def main():
     ap.add_argument("--workload", default="prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode-graph", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--paths", default="staged,direct,direct-expert-major",
                     help="paths to time (staged, direct, staged-expert-major, direct-expert-major); "
                          "the first one gives the headline value")
