@@ -93,9 +93,16 @@ def main():
                          "the first one gives the headline value")
     ap.add_argument("--profile-summary", nargs="+", metavar="DB",
                     help="print per-kernel statistics of rocprofv3 database(s) and exit (no GPU)")
+    ap.add_argument("--api-summary", nargs="+", metavar="DB",
+                    help="print HIP API call counts of rocprofv3 database(s) and exit (no GPU)")
+    ap.add_argument("--decode-graph-only", type=int, metavar="REPLAYS", default=0,
+                    help="only capture the decode step and replay it REPLAYS times (for API tracing)")
     args = ap.parse_args()
     if args.profile_summary:
         profile_summary(args.profile_summary)
+        return
+    if args.api_summary:
+        api_summary(args.api_summary)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the R virtual ranks live in one GPU's HBM and no "
@@ -111,6 +118,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     paths = [p.strip() for p in args.paths.split(",") if p.strip()]
+    if args.decode_graph_only:
+        print(json.dumps(decode_graph(np, torch, a2av, W, paths[0], replays=args.decode_graph_only)), flush=True)
+        return
     w = W.workload(args.workload)
     log(f"workload {w.describe()}; generating inputs")
     x, ids, gates = W.make_inputs(w)
@@ -253,7 +263,7 @@ def time_path(torch, a2av, w, xt, idt, gt, name, steps, warmup):
     }
 
 
-def decode_graph(np, torch, a2av, W, path, steps=100):
+def decode_graph(np, torch, a2av, W, path, steps=100, replays=None):
     """Decode shape: one hipGraph of router stand-in -> dispatch -> expert -> combine,
     replayed `steps` times with fresh routing taken on the device; one event pair around
     all replays, no host synchronisation between them."""
@@ -298,20 +308,26 @@ def decode_graph(np, torch, a2av, W, path, steps=100):
         torch.cuda.synchronize()
         return graph
 
+    nrep = replays or steps
+
     def replay_us(graph):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        for _ in range(steps):
+        for _ in range(nrep):
             graph.replay()
         e1.record()
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / steps
+        return e0.elapsed_time(e1) * 1e3 / nrep
 
     g = capture(step)
-    gh = capture(harness_only)
+    gh = capture(harness_only) if replays is None else None
     counter.zero_()
     us = replay_us(g)
-    ok = int(counter.item()) == steps and int(s.status.item()) == 0
+    ok = int(counter.item()) == nrep and int(s.status.item()) == 0
+    if replays is not None:
+        s.close()
+        return {"workload": w.describe(), "path": path, "replays": nrep, "us_per_step": round(us, 2),
+                "counter_ok": ok}
     us_h = replay_us(gh)
     out = {"workload": w.describe(), "replays": steps, "us_per_step_with_expert_and_router": round(us, 2),
            "us_router_and_expert_only": round(us_h, 2),
@@ -364,6 +380,21 @@ def _short_kernel_name(name):
     base = name.replace("void ", "").replace("a2av::(anonymous namespace)::", "")
     base = base.replace("unsigned int __vector(4)", "u32x4").replace("unsigned int __vector(2)", "u32x2")
     return base.split("(")[0]
+
+
+def api_summary(paths):
+    """HIP runtime API calls per function from rocprofv3 databases (--hip-trace)."""
+    import sqlite3
+    for path in paths:
+        c = sqlite3.connect(path)
+        rows = c.execute("select name, count(*) from regions where category like '%HIP%' "
+                         "group by name order by count(*) desc").fetchall()
+        print(f"# {os.path.basename(path)}")
+        print("| HIP API call | calls |")
+        print("|---|---:|")
+        for name, n in rows:
+            print(f"| {name} | {n} |")
+        print()
 
 
 def profile_summary(paths):
