@@ -12,8 +12,8 @@ dispatch+combine time from HIP events recorded between the library's kernels on 
 stream they run on; `us_per_step` is that time; `ms_per_step` is the wall time of a
 whole step (expert stand-in included) between two synchronisations.  `roofline` is for
 the slowest kernel of the step; `cpu_baseline` is the CPU oracle on a bounded sample of
-the same workload; `decode_graph` is the decode shape captured in a hipGraph and
-replayed with routing that changes on the device each step.
+the same workload; `decode_graph` and `edge_graph` are the decode and edge shapes
+captured in hipGraphs and replayed with routing that changes on the device each step.
 """
 import argparse
 import json
@@ -189,6 +189,7 @@ def main():
 
     if not args.no_decode_graph:
         result["decode_graph"] = {p: decode_graph(np, torch, a2av, W, p) for p in paths}
+        result["edge_graph"] = {p: decode_graph(np, torch, a2av, W, p, workload="edge") for p in paths}
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(np, W, w, args.cpu_sample_tokens)
@@ -263,17 +264,27 @@ def time_path(torch, a2av, w, xt, idt, gt, name, steps, warmup):
     }
 
 
-def decode_graph(np, torch, a2av, W, path, steps=100, replays=None):
-    """Decode shape: one hipGraph of router stand-in -> dispatch -> expert -> combine,
-    replayed `steps` times with fresh routing taken on the device; one event pair around
-    all replays, no host synchronisation between them."""
-    w = W.workload("decode")
-    log(f"decode graph ({path}): {w.describe()}, {steps} replays")
+def decode_graph(np, torch, a2av, W, path, workload="decode", steps=100, per_graph=10, replays=None):
+    """A latency-bound shape captured in hipGraphs and replayed with routing that changes
+    on the device every step (router stand-in -> dispatch -> expert stand-in -> combine),
+    one event pair around all replays and no host synchronisation between them.
+
+    Each graph holds `per_graph` consecutive steps, so the per-step time is GPU time and
+    not the host's graph-launch rate (a one-step graph is also timed: that figure
+    includes the launch rate).  The dispatch+combine share is the full step minus a graph
+    of the router and expert stand-ins alone; the combine therefore reads rows that
+    another kernel has just written, as it would after a real expert.  The flushed
+    variant writes 512 MiB before every step, so each step starts with its inputs out of
+    the 256 MiB last-level cache.  With `replays`, only the one-step graph is captured
+    and replayed that many times (for API tracing)."""
+    w = W.workload(workload)
+    log(f"graph latency ({path}): {w.describe()}, {steps} steps")
     x = W.make_x(w)
     n = w.tokens * w.top_k
     ids_table = torch.from_numpy(np.stack([W.make_ids(w, i).reshape(n) for i in range(steps)])).cuda()
     gates_table = torch.from_numpy(np.stack([W.make_gates(w, i).reshape(n) for i in range(steps)])).cuda()
-    xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    xt = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16) if w.dtype == W.BF16
+          else torch.from_numpy(x)).cuda()
     counter = torch.zeros(1, dtype=torch.int32, device="cuda")
     ids = torch.empty((w.num_ranks, w.tokens_per_rank, w.top_k), dtype=torch.int32, device="cuda")
     gates = torch.empty((w.num_ranks, w.tokens_per_rank, w.top_k), dtype=torch.float32, device="cuda")
@@ -281,19 +292,33 @@ def decode_graph(np, torch, a2av, W, path, steps=100, replays=None):
     path_id, layout = path_config(a2av, path)
     s = a2av.Session(w.num_ranks, w.tokens_per_rank, w.hidden, w.dtype, w.experts_per_rank, w.top_k,
                      path=path_id, recv_layout=layout)
+    flush_buf = None
 
-    def step():
+    def route():
         a2av.a2av_route_step(ids_table, gates_table, steps, n, counter, ids, gates)
+
+    def full():
+        route()
         s.dispatch(xt, ids)
         s.expert(s.recv, s.recv, w.expert_mode)
         s.combine(s.recv, gates, y)
 
-    def harness_only():
+    def harness():
         # the router and expert stand-ins alone (the expert reuses the last routing)
-        a2av.a2av_route_step(ids_table, gates_table, steps, n, counter, ids, gates)
+        route()
         s.expert(s.recv, s.recv, w.expert_mode)
 
-    def capture(fn):
+    def route_dispatch():
+        route()
+        s.dispatch(xt, ids)
+
+    def flushed(fn):
+        def g():
+            flush_buf.fill_(1)
+            fn()
+        return g
+
+    def capture(fn, count):
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -302,41 +327,61 @@ def decode_graph(np, torch, a2av, W, path, steps=100, replays=None):
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            fn()
-        for _ in range(10):
+            for _ in range(count):
+                fn()
+        for _ in range(3):
             graph.replay()
         torch.cuda.synchronize()
         return graph
 
-    nrep = replays or steps
+    def us_per_step(fn, count, total):
+        """Median over 5 trials of (time of total/count replays) / total."""
+        graph = capture(fn, count)
+        trials = []
+        for _ in range(5):
+            counter.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(total // count):
+                graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            if int(counter.item()) != total:
+                raise RuntimeError("router stand-in did not run once per step")
+            trials.append(e0.elapsed_time(e1) * 1e3 / total)
+        del graph
+        return float(np.median(trials))
 
-    def replay_us(graph):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(nrep):
-            graph.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / nrep
-
-    g = capture(step)
-    gh = capture(harness_only) if replays is None else None
-    counter.zero_()
-    us = replay_us(g)
-    ok = int(counter.item()) == nrep and int(s.status.item()) == 0
     if replays is not None:
+        us = us_per_step(full, 1, replays)
+        ok = int(s.status.item()) == 0
         s.close()
-        return {"workload": w.describe(), "path": path, "replays": nrep, "us_per_step": round(us, 2),
+        return {"workload": w.describe(), "path": path, "replays": replays, "us_per_step": round(us, 2),
                 "counter_ok": ok}
-    us_h = replay_us(gh)
-    out = {"workload": w.describe(), "replays": steps, "us_per_step_with_expert_and_router": round(us, 2),
-           "us_router_and_expert_only": round(us_h, 2),
-           "us_dispatch_combine_estimate": round(us - us_h, 2),
-           "host_syncs_between_replays": 0, "counter_ok": ok,
+    t_full = us_per_step(full, per_graph, steps)
+    t_harness = us_per_step(harness, per_graph, steps)
+    t_route = us_per_step(route, per_graph, steps)
+    t_route_dispatch = us_per_step(route_dispatch, per_graph, steps)
+    t_one = us_per_step(full, 1, steps)
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    t_full_f = us_per_step(flushed(full), per_graph, steps)
+    t_harness_f = us_per_step(flushed(harness), per_graph, steps)
+    ok = int(s.status.item()) == 0
+    out = {"workload": w.describe(), "steps": steps, "steps_per_graph": per_graph,
+           "us_per_step_with_expert_and_router": round(t_full, 2),
+           "us_router_and_expert_only": round(t_harness, 2),
+           "us_dispatch_combine_estimate": round(t_full - t_harness, 2),
+           "us_dispatch_only_estimate": round(t_route_dispatch - t_route, 2),
+           "us_per_step_one_step_graphs": round(t_one, 2),
+           "flushed_512MiB": {"us_per_step_with_expert_and_router": round(t_full_f, 2),
+                              "us_router_and_expert_only": round(t_harness_f, 2),
+                              "us_dispatch_combine_estimate": round(t_full_f - t_harness_f, 2)},
+           "host_syncs_between_replays": 0, "status_ok": ok,
            "algorithmic_bytes_per_step": step_bytes(w, path_id == a2av.PATH_DIRECT)}
-    del gh
+    log(f"graph latency ({path}, {workload}): dispatch+combine {t_full - t_harness:.2f} us warm, "
+        f"{t_full_f - t_harness_f:.2f} us flushed")
+    del flush_buf
     s.close()
-    del g
     torch.cuda.empty_cache()
     return out
 

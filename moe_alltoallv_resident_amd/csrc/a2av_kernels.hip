@@ -150,8 +150,10 @@ __device__ void write_recv_tables(const Shape& sh, const Tables& tb, const Outpu
     }
 }
 
-// Blocks that build the receive tables come first in the grid of the kernel that
-// follows planning: one wavefront per receiver.
+// Blocks that build the receive tables, one wavefront per receiver, in the grid of the
+// kernel that follows planning: after the row blocks in pack (so that pack's row blocks
+// keep the same block numbers as those of the kernels reading its rows), first in the
+// bare collective.
 __host__ __device__ __forceinline__ int64_t table_blocks(int R) { return (R + kRowsPerBlock - 1) / kRowsPerBlock; }
 
 // ------------------------------------------------------------------------------------
@@ -266,35 +268,37 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanArgs a) {
 }
 
 // Expert-major receive places.  Receiver d's rows are grouped by local expert, then by
-// sender, then in the sender's order.  One wavefront per receiver; lane l owns d's local
-// experts l, l+64, ...: it sums its expert's column of cnt over the senders (loads issued
-// together), a wavefront scan of those totals gives where each expert's group starts
-// (recv_eoff), and a second walk over the senders gives xbase[s][e], the place of the
-// first row s sends to e.
+// sender, then in the sender's order, so the place of the first row sender s sends to
+// expert e is the sum of cnt[s'][e'] over the (local expert, sender) pairs before (e, s)
+// in that order: an exclusive scan over d's epr x R pairs.  One wavefront per receiver;
+// lane l takes pair c0 + l of each run of 64, the run's counts are loaded together (the
+// next run's while this one is scanned), and a wavefront scan with a carry between runs
+// gives xbase[s][e] and, at each expert's first sender, recv_eoff[d][le].
 __global__ void __launch_bounds__(kBlock) layout_kernel(Shape sh, Tables tb) {
     const int lane = lane_id();
     const int d = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
     if (d >= sh.R) return;
     const int R = sh.R, E = sh.E, epr = sh.epr;
+    const int pairs = epr * R;   // = E
+    auto load = [&](int i) -> int {
+        if (i >= pairs) return 0;
+        const int le = i / R, s = i - le * R;
+        return tb.cnt[(int64_t)s * E + d * epr + le];
+    };
     int carry = 0;
-    for (int l0 = 0; l0 < epr; l0 += kWave) {
-        const int le = l0 + lane;
-        const bool mine = le < epr;
-        const int e = d * epr + le;
-        int total = 0;
-        if (mine)
-            for (int s = 0; s < R; ++s) total += tb.cnt[(int64_t)s * E + e];
-        const int incl = wave_inclusive_scan(total);
-        const int start = carry + incl - total;
-        if (mine) {
-            tb.recv_eoff[(int64_t)d * (epr + 1) + le] = start;
-            int run = start;
-            for (int s = 0; s < R; ++s) {
-                tb.xbase[(int64_t)s * E + e] = run;
-                run += tb.cnt[(int64_t)s * E + e];
-            }
+    int c = load(lane);
+    for (int c0 = 0; c0 < pairs; c0 += kWave) {
+        const int next = load(c0 + kWave + lane);
+        const int i = c0 + lane;
+        const int incl = wave_inclusive_scan(c);
+        if (i < pairs) {
+            const int le = i / R, s = i - le * R;
+            const int start = carry + incl - c;
+            tb.xbase[(int64_t)s * E + d * epr + le] = start;
+            if (s == 0) tb.recv_eoff[(int64_t)d * (epr + 1) + le] = start;
         }
         carry += __shfl(incl, kWave - 1, kWave);
+        c = next;
     }
     if (lane == 0) tb.recv_eoff[(int64_t)d * (epr + 1) + epr] = carry;
 }
@@ -402,18 +406,18 @@ __device__ __forceinline__ int segment_of(const int32_t* so, int R, int64_t p, i
 }
 
 // pack: row x[s][t] to its k places: the sender's send buffer (staged) or the
-// receivers' buffers (direct).  The first blocks build the receive tables.
+// receivers' buffers (direct).  The blocks after the row blocks build the receive tables.
 template <typename V, int U, bool NT, bool DIRECT>
 __global__ void __launch_bounds__(kBlock) pack_kernel(const V* __restrict__ x, V* __restrict__ dst, Shape sh,
                                                       Tables tb, Outputs out, uint32_t* status, Split sp) {
     const int lane = lane_id();
-    const int64_t tblk = table_blocks(sh.R);
-    if ((int64_t)blockIdx.x < tblk) {
-        const int d = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
-        if (d < sh.R) write_recv_tables(sh, tb, out, status, d, lane);
+    const int64_t rblk = ((int64_t)sh.R * sh.T * sp.cpr + kRowsPerBlock - 1) / kRowsPerBlock;
+    if ((int64_t)blockIdx.x >= rblk) {
+        const int64_t d = ((int64_t)blockIdx.x - rblk) * kRowsPerBlock + threadIdx.x / kWave;
+        if (d < sh.R) write_recv_tables(sh, tb, out, status, (int)d, lane);
         return;
     }
-    const Piece pc = piece_of(((int64_t)blockIdx.x - tblk) * kRowsPerBlock + threadIdx.x / kWave, sp);
+    const Piece pc = piece_of((int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kWave, sp);
     const int64_t n = pc.row;
     if (n >= (int64_t)sh.R * sh.T) return;
     const int64_t s = n / sh.T;
@@ -453,26 +457,65 @@ __global__ void __launch_bounds__(kBlock) pack_kernel(const V* __restrict__ x, V
     }
 }
 
-// exchange (staged path): send row (s, p) <-> receive row (d, q).  Forward copies send
-// -> recv and drops rows past the capacity; reverse copies recv-layout expert outputs
-// back to the send places and writes zeros where a row was dropped.  FIRST: this is the
-// first kernel after planning (the bare collective), so the first blocks build the
-// receive tables and rows find their receive offset from the send offsets.
-template <typename V, int U, bool NT, bool REVERSE, bool FIRST>
+// exchange (staged path), in token order: for token row n of sender s and each slot j,
+// send place p = pos[n][j] <-> receive row (d, q).  Forward copies send -> recv and
+// drops rows past the capacity; reverse copies the recv-layout expert outputs back to
+// the send places and writes zeros where a row was dropped.  Rows are taken by token
+// with the same row-to-block map as pack and combine: blocks are spread over the XCDs
+// round-robin by block number and each XCD has its own L2, so a row is read on the XCD
+// that wrote it (pack -> exchange, reverse exchange -> combine), which at decode sizes
+// is markedly faster than reading a row another XCD has just written.
+template <typename V, int U, bool NT, bool REVERSE>
 __global__ void __launch_bounds__(kBlock) exchange_kernel(const V* __restrict__ src, V* __restrict__ dst, Shape sh,
-                                                          Tables tb, Outputs out, uint32_t* status, Split sp) {
+                                                          Tables tb, Split sp) {
     const int lane = lane_id();
-    int64_t blk = blockIdx.x;
-    if constexpr (FIRST) {
-        const int64_t tblk = table_blocks(sh.R);
-        if (blk < tblk) {
-            const int d = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
-            if (d < sh.R) write_recv_tables(sh, tb, out, status, d, lane);
-            return;
-        }
-        blk -= tblk;
+    const Piece pc = piece_of((int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kWave, sp);
+    const int64_t n = pc.row;
+    if (n >= (int64_t)sh.R * sh.T) return;
+    const int64_t s = n / sh.T;
+    const int k = sh.k, R = sh.R;
+    const int nvec = sp.nvec;
+    const int my_p = lane < k ? tb.pos[n * k + lane] : -1;
+    const int32_t* so = tb.send_off + s * (R + 1);
+    // lane j: slot j's receive row, or -1 past the capacity, or -2 if the slot has no place
+    int64_t my_q = -2;
+    for (int j = 0; j < k; ++j) {
+        const int pj = __builtin_amdgcn_readlane(my_p, j);
+        if (pj < 0 || pj >= sh.TK) continue;
+        const int d = segment_of(so, R, pj, lane);
+        if (d >= R) continue;
+        const int64_t q = sh.layout ? expert_major_place(sh, tb, s, pj, d, lane)
+                                    : (int64_t)tb.recv_off[(int64_t)d * (R + 1) + s] + (pj - so[d]);
+        if (lane == j) my_q = (q >= 0 && q < sh.cap) ? (int64_t)d * sh.cap + q : -1;
     }
-    const Piece pc = piece_of(blk * kRowsPerBlock + threadIdx.x / kWave, sp);
+    for (int j = 0; j < k; ++j) {
+        const int64_t rj = __shfl(my_q, j, kWave);
+        if (rj == -2) continue;
+        const int64_t send_row = s * sh.TK + __builtin_amdgcn_readlane(my_p, j);
+        if (!REVERSE) {
+            if (rj >= 0) copy_row<V, U, NT>(dst + rj * nvec, src + send_row * nvec, pc.v0, pc.v1, lane);
+        } else if (rj >= 0) {
+            copy_row<V, U, NT>(dst + send_row * nvec, src + rj * nvec, pc.v0, pc.v1, lane);
+        } else {
+            zero_row<V>(dst + send_row * nvec, pc.v0, pc.v1, lane);
+        }
+    }
+}
+
+// The bare collective (no plan, no positions): send row (s, p) -> receive row (d, q) in
+// send order.  This is the first kernel after the counts are taken, so the first blocks
+// build the receive tables and rows find their receive offset from the send offsets.
+template <typename V, int U, bool NT>
+__global__ void __launch_bounds__(kBlock) alltoallv_kernel(const V* __restrict__ src, V* __restrict__ dst, Shape sh,
+                                                           Tables tb, Outputs out, uint32_t* status, Split sp) {
+    const int lane = lane_id();
+    const int64_t tblk = table_blocks(sh.R);
+    if ((int64_t)blockIdx.x < tblk) {
+        const int d = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
+        if (d < sh.R) write_recv_tables(sh, tb, out, status, d, lane);
+        return;
+    }
+    const Piece pc = piece_of(((int64_t)blockIdx.x - tblk) * kRowsPerBlock + threadIdx.x / kWave, sp);
     const int64_t g = pc.row;
     if (g >= (int64_t)sh.R * sh.TK) return;
     const int R = sh.R;
@@ -481,19 +524,9 @@ __global__ void __launch_bounds__(kBlock) exchange_kernel(const V* __restrict__ 
     const int32_t* so = tb.send_off + s * (R + 1);
     if (p >= so[R]) return;
     const int d = segment_of(so, R, p, lane);
-    int64_t q;
-    if (FIRST) q = recv_base(tb.send_off, R, d, (int)s, lane) + (p - so[d]);   // the bare collective
-    else if (sh.layout) q = expert_major_place(sh, tb, s, p, d, lane);
-    else q = (int64_t)tb.recv_off[(int64_t)d * (R + 1) + s] + (p - so[d]);
-    const int64_t send_row = s * sh.TK + p, recv_row = (int64_t)d * sh.cap + q;
-    const bool in_cap = q >= 0 && q < sh.cap;
-    if (!REVERSE) {
-        if (!in_cap) return;
-        copy_row<V, U, NT>(dst + recv_row * nvec, src + send_row * nvec, pc.v0, pc.v1, lane);
-    } else {
-        if (!in_cap) { zero_row<V>(dst + send_row * nvec, pc.v0, pc.v1, lane); return; }
-        copy_row<V, U, NT>(dst + send_row * nvec, src + recv_row * nvec, pc.v0, pc.v1, lane);
-    }
+    const int64_t q = recv_base(tb.send_off, R, d, (int)s, lane) + (p - so[d]);
+    if (q < 0 || q >= sh.cap) return;
+    copy_row<V, U, NT>(dst + ((int64_t)d * sh.cap + q) * nvec, src + g * nvec, pc.v0, pc.v1, lane);
 }
 
 // ---- element access for the arithmetic kernels --------------------------------------
@@ -809,11 +842,13 @@ hipError_t launch_pack(const Shape& sh, const Tables& tb, const Outputs& out, ui
 
 hipError_t launch_exchange(const Shape& sh, const Tables& tb, const Outputs& out, uint32_t* status, const void* src,
                            void* dst, bool reverse, bool first, int vec, hipStream_t st) {
-    const int64_t rows = (int64_t)sh.R * sh.TK;
+    // token order (one piece per token row, the split of pack and combine), or send
+    // order for the bare collective
+    const int64_t rows = first ? (int64_t)sh.R * sh.TK : (int64_t)sh.R * sh.T;
     const Split sp = make_split(sh.row_bytes, vec, rows, sh.num_cu);
     const unsigned grid = (unsigned)((first ? table_blocks(sh.R) : 0) + piece_blocks(rows, sp));
     if (grid == 0) return hipSuccess;
-    const int64_t bytes = rows * sh.row_bytes;
+    const int64_t bytes = (int64_t)sh.R * sh.TK * sh.row_bytes;
     return with_vec(vec, [&](auto B) {
         using V = typename Vec<decltype(B)::value>::T;
         return with_unroll(sp.cv, [&](auto U) {
@@ -821,14 +856,14 @@ hipError_t launch_exchange(const Shape& sh, const Tables& tb, const Outputs& out
                 constexpr int u = decltype(U)::value;
                 constexpr bool nt = decltype(NT)::value;
                 if (first)
-                    hipLaunchKernelGGL((exchange_kernel<V, u, nt, false, true>), dim3(grid), dim3(kBlock), 0, st,
-                                       (const V*)src, (V*)dst, sh, tb, out, status, sp);
+                    hipLaunchKernelGGL((alltoallv_kernel<V, u, nt>), dim3(grid), dim3(kBlock), 0, st, (const V*)src,
+                                       (V*)dst, sh, tb, out, status, sp);
                 else if (reverse)
-                    hipLaunchKernelGGL((exchange_kernel<V, u, nt, true, false>), dim3(grid), dim3(kBlock), 0, st,
-                                       (const V*)src, (V*)dst, sh, tb, out, status, sp);
+                    hipLaunchKernelGGL((exchange_kernel<V, u, nt, true>), dim3(grid), dim3(kBlock), 0, st,
+                                       (const V*)src, (V*)dst, sh, tb, sp);
                 else
-                    hipLaunchKernelGGL((exchange_kernel<V, u, nt, false, false>), dim3(grid), dim3(kBlock), 0, st,
-                                       (const V*)src, (V*)dst, sh, tb, out, status, sp);
+                    hipLaunchKernelGGL((exchange_kernel<V, u, nt, false>), dim3(grid), dim3(kBlock), 0, st,
+                                       (const V*)src, (V*)dst, sh, tb, sp);
                 return hipGetLastError();
             });
         });
