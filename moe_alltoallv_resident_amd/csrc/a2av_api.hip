@@ -228,16 +228,24 @@ int a2av_dispatch(a2av_handle_t h, const void* x, const int32_t* topk_ids, void*
     hipStream_t st = static_cast<hipStream_t>(stream);
     const a2av::Outputs out{split, recv_counts, recv_offsets};
     const a2av::Tables& tb = h->tb;
-    int rc = launch_timed(h, kStagePlan, st, [&] { return a2av::launch_plan(sh, tb, topk_ids, out, status, st); });
-    if (rc != A2AV_OK) return rc;
-    if (sh.layout == A2AV_LAYOUT_EXPERT_MAJOR) {
-        rc = launch_timed(h, kStagePlan, st, [&] { return a2av::launch_layout(sh, tb, st); });
+    void* dst = h->direct ? recv : h->send_buf;
+    int rc;
+    if (a2av::small_dispatch(sh)) {
+        rc = launch_timed(h, kStagePack, st, [&] {
+            return a2av::launch_dispatch_small(sh, tb, topk_ids, out, status, x, dst, h->direct, vec, st);
+        });
+        if (rc != A2AV_OK) return rc;
+    } else {
+        rc = launch_timed(h, kStagePlan, st, [&] { return a2av::launch_plan(sh, tb, topk_ids, out, status, st); });
+        if (rc != A2AV_OK) return rc;
+        if (sh.layout == A2AV_LAYOUT_EXPERT_MAJOR) {
+            rc = launch_timed(h, kStagePlan, st, [&] { return a2av::launch_layout(sh, tb, st); });
+            if (rc != A2AV_OK) return rc;
+        }
+        rc = launch_timed(h, kStagePack, st,
+                          [&] { return a2av::launch_pack(sh, tb, out, status, x, dst, h->direct, vec, st); });
         if (rc != A2AV_OK) return rc;
     }
-    void* dst = h->direct ? recv : h->send_buf;
-    rc = launch_timed(h, kStagePack, st,
-                      [&] { return a2av::launch_pack(sh, tb, out, status, x, dst, h->direct, vec, st); });
-    if (rc != A2AV_OK) return rc;
     if (!h->direct && sh.TK > 0) {
         rc = launch_timed(h, kStageExchange, st, [&] {
             return a2av::launch_exchange(sh, tb, out, status, h->send_buf, recv, false, false, vec, st);

@@ -55,6 +55,11 @@ hipError_t launch_plan(const Shape& sh, const Tables& tb, const int32_t* ids, co
 hipError_t launch_layout(const Shape& sh, const Tables& tb, hipStream_t st);
 hipError_t launch_plan_from_counts(const Shape& sh, const Tables& tb, const int32_t* send_counts,
                                    uint32_t* status, hipStream_t st);
+// Small steps (decode sizes): planning, receiver tables (and expert-major places) and
+// the pack in one launch in which every block works from the ids alone.
+bool small_dispatch(const Shape& sh);
+hipError_t launch_dispatch_small(const Shape& sh, const Tables& tb, const int32_t* ids, const Outputs& out,
+                                 uint32_t* status, const void* x, void* dst, bool direct, int vec, hipStream_t st);
 // pack: staged (dst = send buffer) or direct (dst = receive buffer); also builds the
 // receive tables (and the caller's copies in `out`).
 hipError_t launch_pack(const Shape& sh, const Tables& tb, const Outputs& out, uint32_t* status, const void* x,

@@ -176,14 +176,12 @@ struct PlanArgs {
     uint32_t* status;
 };
 
+// Planning of rank s by the whole block; lds holds (waves + 1) * E ints, wsum 17.
 template <int S>
-__global__ void __launch_bounds__(1024) plan_kernel(PlanArgs a) {
-    extern __shared__ int lds[];
-    __shared__ int wsum[17];
+__device__ void plan_rank(const PlanArgs& a, int s, int* lds, int* wsum) {
     const Shape& sh = a.sh;
     const int E = sh.E, R = sh.R;
     const int tid = threadIdx.x, nt = blockDim.x, lane = lane_id(), w = tid / kWave, nw = nt / kWave;
-    const int s = blockIdx.x;
     int* cw = lds;               // [nw][E] per-wavefront counters, later bases
     int* tot = lds + nw * E;     // [E] per-expert totals, later exclusive offsets
 
@@ -265,6 +263,13 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanArgs a) {
             pos[i] = (e >= 0 && e < E) ? mine[e] + pos[i] : -1;
         }
     }
+}
+
+template <int S>
+__global__ void __launch_bounds__(1024) plan_kernel(PlanArgs a) {
+    extern __shared__ int lds[];
+    __shared__ int wsum[17];
+    plan_rank<S>(a, blockIdx.x, lds, wsum);
 }
 
 // Expert-major receive places.  Receiver d's rows are grouped by local expert, then by
@@ -457,65 +462,243 @@ __global__ void __launch_bounds__(kBlock) pack_kernel(const V* __restrict__ x, V
     }
 }
 
-// exchange (staged path), in token order: for token row n of sender s and each slot j,
-// send place p = pos[n][j] <-> receive row (d, q).  Forward copies send -> recv and
-// drops rows past the capacity; reverse copies the recv-layout expert outputs back to
-// the send places and writes zeros where a row was dropped.  Rows are taken by token
-// with the same row-to-block map as pack and combine: blocks are spread over the XCDs
-// round-robin by block number and each XCD has its own L2, so a row is read on the XCD
-// that wrote it (pack -> exchange, reverse exchange -> combine), which at decode sizes
-// is markedly faster than reading a row another XCD has just written.
-template <typename V, int U, bool NT, bool REVERSE>
-__global__ void __launch_bounds__(kBlock) exchange_kernel(const V* __restrict__ src, V* __restrict__ dst, Shape sh,
-                                                          Tables tb, Split sp) {
-    const int lane = lane_id();
-    const Piece pc = piece_of((int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kWave, sp);
-    const int64_t n = pc.row;
-    if (n >= (int64_t)sh.R * sh.T) return;
-    const int64_t s = n / sh.T;
-    const int k = sh.k, R = sh.R;
-    const int nvec = sp.nvec;
-    const int my_p = lane < k ? tb.pos[n * k + lane] : -1;
-    const int32_t* so = tb.send_off + s * (R + 1);
-    // lane j: slot j's receive row, or -1 past the capacity, or -2 if the slot has no place
-    int64_t my_q = -2;
-    for (int j = 0; j < k; ++j) {
-        const int pj = __builtin_amdgcn_readlane(my_p, j);
-        if (pj < 0 || pj >= sh.TK) continue;
-        const int d = segment_of(so, R, pj, lane);
-        if (d >= R) continue;
-        const int64_t q = sh.layout ? expert_major_place(sh, tb, s, pj, d, lane)
-                                    : (int64_t)tb.recv_off[(int64_t)d * (R + 1) + s] + (pj - so[d]);
-        if (lane == j) my_q = (q >= 0 && q < sh.cap) ? (int64_t)d * sh.cap + q : -1;
+// ---- one-launch dispatch for small steps -------------------------------------------
+// At decode sizes the step is short enough that every dependent read of a table just
+// written by another kernel shows: such a table sits in another XCD's L2 or in HBM,
+// and the read costs microseconds.  So a small step's dispatch is one launch in which
+// no block reads what another block of the launch writes; every block works from the
+// routing ids directly:
+//   blocks [0, R)          planning of one rank each (the tables later kernels use);
+//   next table_blocks(R)   receiver tables, counted from the ids;
+//   from `lead` on         rows: each wavefront finds where its token's k assignments
+//                          go by counting the assignments that come before them in the
+//                          destination's order, and copies the row there.
+// `lead` is a multiple of 8, so a row keeps the block number (and with it the XCD) it
+// has in the combine.
+
+// The step's ids, copied into LDS by the whole block (one round of loads).
+__device__ __forceinline__ void stage_ids(const int32_t* __restrict__ ids, int64_t A, int* sids) {
+#pragma unroll 4
+    for (int64_t i = threadIdx.x; i < A; i += blockDim.x) sids[i] = ids[i];
+}
+
+// Places of NS assignments of one token row of sender s in their destinations' order,
+// counted over the ids (in LDS) by the whole wavefront in one pass, one ballot per slot
+// per 64 ids (the counts are wavefront-uniform).  Assignment j has index me0 + j, expert
+// e[j] (< 0: none) and destination d[j].  Staged: its place in the sender's (expert,
+// token, slot) order.  Direct, source-major: rows d gets from the senders before s, then
+// s's rows for d's experts below e, then s's earlier rows for e.  Direct, expert-major:
+// d's rows for its experts below e, then the earlier rows for e over all senders in
+// (sender, token, slot) order.
+template <bool DIRECT, int NS>
+__device__ __forceinline__ void count_places(const Shape& sh, const int* sids, int s, int me0, const int* e,
+                                             const int* d, int* q, int lane) {
+    const int A = sh.R * (int)sh.TK, TK = (int)sh.TK;
+    int lo, hi, before;       // ids scanned, and the index below which every row of d counts
+    if (!DIRECT) { lo = s * TK; hi = lo + TK; before = lo; }
+    else if (sh.layout) { lo = 0; hi = A; before = 0; }
+    else { lo = 0; hi = (s + 1) * TK; before = s * TK; }
+    int elo[NS], ehi[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        elo[j] = e[j] >= 0 ? (DIRECT ? d[j] * sh.epr : 0) : 1;
+        ehi[j] = e[j] >= 0 ? (DIRECT ? elo[j] + sh.epr : sh.E) : 0;   // empty range: counts nothing
+        q[j] = 0;
     }
-    for (int j = 0; j < k; ++j) {
-        const int64_t rj = __shfl(my_q, j, kWave);
-        if (rj == -2) continue;
-        const int64_t send_row = s * sh.TK + __builtin_amdgcn_readlane(my_p, j);
-        if (!REVERSE) {
-            if (rj >= 0) copy_row<V, U, NT>(dst + rj * nvec, src + send_row * nvec, pc.v0, pc.v1, lane);
-        } else if (rj >= 0) {
-            copy_row<V, U, NT>(dst + send_row * nvec, src + rj * nvec, pc.v0, pc.v1, lane);
-        } else {
-            zero_row<V>(dst + send_row * nvec, pc.v0, pc.v1, lane);
+    constexpr int kRuns = 4;   // 64-id runs read before any is used
+    for (int i0 = lo; i0 < hi; i0 += kRuns * kWave) {
+        int v[kRuns];
+#pragma unroll
+        for (int u = 0; u < kRuns; ++u) {
+            const int i = i0 + u * kWave + lane;
+            v[u] = sids[i < hi ? i : lo];
+        }
+#pragma unroll
+        for (int u = 0; u < kRuns; ++u) {
+            const int i = i0 + u * kWave + lane;
+#pragma unroll
+            for (int j = 0; j < NS; ++j) {
+                const bool hit = i < hi && v[u] >= elo[j] && v[u] < ehi[j] &&
+                                 (i < before || v[u] < e[j] || (v[u] == e[j] && i < me0 + j));
+                q[j] += __popcll(__ballot(hit));
+            }
         }
     }
 }
 
-// The bare collective (no plan, no positions): send row (s, p) -> receive row (d, q) in
-// send order.  This is the first kernel after the counts are taken, so the first blocks
-// build the receive tables and rows find their receive offset from the send offsets.
-template <typename V, int U, bool NT>
-__global__ void __launch_bounds__(kBlock) alltoallv_kernel(const V* __restrict__ src, V* __restrict__ dst, Shape sh,
-                                                           Tables tb, Outputs out, uint32_t* status, Split sp) {
-    const int lane = lane_id();
-    const int64_t tblk = table_blocks(sh.R);
-    if ((int64_t)blockIdx.x < tblk) {
-        const int d = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
-        if (d < sh.R) write_recv_tables(sh, tb, out, status, d, lane);
+// Receiver d's tables counted from the ids (in LDS) by one wavefront into `hist`
+// (epr x R ints of LDS, zeroed by the caller): hist[le * R + s] = rows sender s sends to
+// d's local expert le, by LDS atomic increments.  count_tables_write then forms
+// recv_counts / recv_off as write_recv_tables does and, for expert-major buffers, xbase
+// and recv_eoff as layout_kernel does; the caller puts a block barrier between the two.
+__device__ __forceinline__ void count_tables_fill(const Shape& sh, const int* sids, int d, int lane, int* hist) {
+    const int A = sh.R * (int)sh.TK, TK = (int)sh.TK;
+    const int elo = d * sh.epr;
+    for (int i = lane; i < A; i += kWave) {
+        const int le = sids[i] - elo;
+        if (le >= 0 && le < sh.epr) atomicAdd(&hist[le * sh.R + i / TK], 1);
+    }
+}
+
+__device__ void count_tables_write(const Shape& sh, const Tables& tb, const Outputs& out, uint32_t* status, int d,
+                                   int lane, const int* hist) {
+    const int R = sh.R, E = sh.E, epr = sh.epr;
+    int carry = 0;
+    for (int s0 = 0; s0 < R; s0 += kWave) {
+        const int s = s0 + lane;
+        int c = 0;
+        if (s < R)
+            for (int le = 0; le < epr; ++le) c += hist[le * R + s];
+        const int incl = wave_inclusive_scan(c);
+        if (s < R) {
+            const int off = carry + incl - c;
+            tb.recv_counts[(int64_t)d * R + s] = c;
+            tb.recv_off[(int64_t)d * (R + 1) + s] = off;
+            if (out.recv_counts) out.recv_counts[(int64_t)d * R + s] = c;
+            if (out.recv_off) out.recv_off[(int64_t)d * (R + 1) + s] = off;
+        }
+        carry += __shfl(incl, kWave - 1, kWave);
+    }
+    if (lane == 0) {
+        tb.recv_off[(int64_t)d * (R + 1) + R] = carry;
+        if (out.recv_off) out.recv_off[(int64_t)d * (R + 1) + R] = carry;
+        if ((int64_t)carry > sh.cap) atomicOr(status, 2u);
+    }
+    if (!sh.layout) return;
+    // expert-major: exclusive scan over (local expert, sender) pairs, expert-major
+    const int pairs = epr * R;
+    carry = 0;
+    for (int c0 = 0; c0 < pairs; c0 += kWave) {
+        const int i = c0 + lane;
+        const int c = i < pairs ? hist[i] : 0;
+        const int incl = wave_inclusive_scan(c);
+        if (i < pairs) {
+            const int le = i / R, s = i - le * R;
+            const int start = carry + incl - c;
+            tb.xbase[(int64_t)s * E + d * epr + le] = start;
+            if (s == 0) tb.recv_eoff[(int64_t)d * (epr + 1) + le] = start;
+        }
+        carry += __shfl(incl, kWave - 1, kWave);
+    }
+    if (lane == 0) tb.recv_eoff[(int64_t)d * (epr + 1) + epr] = carry;
+}
+
+// LDS (ints) of the one-launch dispatch: planning needs 5 rows of E counters, a table
+// block 4 histograms of E plus the ids, a row block the ids.
+__host__ __device__ __forceinline__ int64_t small_lds_ints(int64_t E, int64_t A) {
+    const int64_t plan = (kRowsPerBlock + 1) * E, tables = kRowsPerBlock * E + A;
+    return plan > tables ? plan : tables;
+}
+
+template <typename V, int U, bool DIRECT>
+__global__ void __launch_bounds__(kBlock) dispatch_small_kernel(const V* __restrict__ x, V* __restrict__ dst,
+                                                                PlanArgs a, Split sp, int lead) {
+    extern __shared__ int lds[];
+    __shared__ int wsum[17];
+    const Shape& sh = a.sh;
+    const int lane = lane_id(), w = threadIdx.x / kWave;
+    const int R = sh.R;
+    const int64_t A = (int64_t)R * sh.TK;
+    if ((int)blockIdx.x < R) {                      // planning of one rank
+        plan_rank<1>(a, blockIdx.x, lds, wsum);
         return;
     }
-    const Piece pc = piece_of(((int64_t)blockIdx.x - tblk) * kRowsPerBlock + threadIdx.x / kWave, sp);
+    if ((int)blockIdx.x < lead) {                   // receiver tables
+        const int64_t d = ((int64_t)blockIdx.x - R) * kRowsPerBlock + w;
+        int* hist = lds + w * sh.E;                 // epr x R = E ints per wavefront
+        int* sids = lds + kRowsPerBlock * sh.E;
+        for (int i = lane; i < sh.E; i += kWave) hist[i] = 0;
+        stage_ids(a.ids, A, sids);
+        __syncthreads();
+        if (d < R) count_tables_fill(sh, sids, (int)d, lane, hist);
+        __syncthreads();
+        if (d < R) count_tables_write(sh, a.tb, a.out, a.status, (int)d, lane, hist);
+        return;
+    }
+    const Piece pc = piece_of(((int64_t)blockIdx.x - lead) * kRowsPerBlock + w, sp);
+    const int64_t n = pc.row;
+    const bool live = n < (int64_t)R * sh.T;
+    const int64_t s = n / sh.T;
+    const int k = sh.k, nvec = sp.nvec;
+    const V* src = x + n * nvec;
+    V r[U];
+    int base = pc.v0;
+    if (live) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int v = base + u * kWave + lane;
+            if (v < pc.v1) r[u] = ld<false>(src + v);
+        }
+    }
+    stage_ids(a.ids, A, lds);
+    __syncthreads();
+    if (!live) return;
+    // lane j: slot j's destination row, -1 if the slot has none
+    int64_t my_row = -1;
+    auto place = [&](auto NSC, int j0) {
+        constexpr int NS = decltype(NSC)::value;
+        int e[NS], d[NS], q[NS];
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            const int v = lds[n * k + j0 + j];
+            e[j] = v >= 0 && v < sh.E ? v : -1;     // out-of-range id: dropped (planning flags it)
+            d[j] = e[j] >= 0 ? e[j] / sh.epr : 0;
+        }
+        count_places<DIRECT, NS>(sh, lds, (int)s, (int)(n * k + j0), e, d, q, lane);
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            if (e[j] < 0) continue;
+            int64_t row;
+            if constexpr (DIRECT) row = q[j] < sh.cap ? (int64_t)d[j] * sh.cap + q[j] : -1;   // past capacity
+            else row = s * sh.TK + q[j];
+            if (lane == j0 + j) my_row = row;
+        }
+    };
+    int j0 = 0;
+    for (; j0 + 4 <= k; j0 += 4) place(std::integral_constant<int, 4>{}, j0);
+    if (k - j0 >= 2) { place(std::integral_constant<int, 2>{}, j0); j0 += 2; }
+    if (k - j0 == 1) place(std::integral_constant<int, 1>{}, j0);
+    for (;;) {
+        for (int j = 0; j < k; ++j) {
+            const int64_t rj = __shfl(my_row, j, kWave);
+            if (rj < 0) continue;
+            V* row = dst + rj * nvec;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int v = base + u * kWave + lane;
+                if (v < pc.v1) st<false>(row + v, r[u]);
+            }
+        }
+        base += kWave * U;
+        if (base >= pc.v1) break;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int v = base + u * kWave + lane;
+            if (v < pc.v1) r[u] = ld<false>(src + v);
+        }
+    }
+}
+
+// exchange (staged path): send row (s, p) <-> receive row (d, q).  Forward copies send
+// -> recv and drops rows past the capacity; reverse copies recv-layout expert outputs
+// back to the send places and writes zeros where a row was dropped.  FIRST: this is the
+// first kernel after planning (the bare collective), so the first blocks build the
+// receive tables and rows find their receive offset from the send offsets.
+template <typename V, int U, bool NT, bool REVERSE, bool FIRST>
+__global__ void __launch_bounds__(kBlock) exchange_kernel(const V* __restrict__ src, V* __restrict__ dst, Shape sh,
+                                                          Tables tb, Outputs out, uint32_t* status, Split sp) {
+    const int lane = lane_id();
+    int64_t blk = blockIdx.x;
+    if constexpr (FIRST) {
+        const int64_t tblk = table_blocks(sh.R);
+        if (blk < tblk) {
+            const int d = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
+            if (d < sh.R) write_recv_tables(sh, tb, out, status, d, lane);
+            return;
+        }
+        blk -= tblk;
+    }
+    const Piece pc = piece_of(blk * kRowsPerBlock + threadIdx.x / kWave, sp);
     const int64_t g = pc.row;
     if (g >= (int64_t)sh.R * sh.TK) return;
     const int R = sh.R;
@@ -524,9 +707,19 @@ __global__ void __launch_bounds__(kBlock) alltoallv_kernel(const V* __restrict__
     const int32_t* so = tb.send_off + s * (R + 1);
     if (p >= so[R]) return;
     const int d = segment_of(so, R, p, lane);
-    const int64_t q = recv_base(tb.send_off, R, d, (int)s, lane) + (p - so[d]);
-    if (q < 0 || q >= sh.cap) return;
-    copy_row<V, U, NT>(dst + ((int64_t)d * sh.cap + q) * nvec, src + g * nvec, pc.v0, pc.v1, lane);
+    int64_t q;
+    if (FIRST) q = recv_base(tb.send_off, R, d, (int)s, lane) + (p - so[d]);   // the bare collective
+    else if (sh.layout) q = expert_major_place(sh, tb, s, p, d, lane);
+    else q = (int64_t)tb.recv_off[(int64_t)d * (R + 1) + s] + (p - so[d]);
+    const int64_t send_row = s * sh.TK + p, recv_row = (int64_t)d * sh.cap + q;
+    const bool in_cap = q >= 0 && q < sh.cap;
+    if (!REVERSE) {
+        if (!in_cap) return;
+        copy_row<V, U, NT>(dst + recv_row * nvec, src + send_row * nvec, pc.v0, pc.v1, lane);
+    } else {
+        if (!in_cap) { zero_row<V>(dst + send_row * nvec, pc.v0, pc.v1, lane); return; }
+        copy_row<V, U, NT>(dst + send_row * nvec, src + recv_row * nvec, pc.v0, pc.v1, lane);
+    }
 }
 
 // ---- element access for the arithmetic kernels --------------------------------------
@@ -840,15 +1033,44 @@ hipError_t launch_pack(const Shape& sh, const Tables& tb, const Outputs& out, ui
     });
 }
 
+bool small_dispatch(const Shape& sh) {
+    // planning fits one 64-assignment batch per wavefront of a 4-wavefront block, each
+    // row wavefront counts over at most 1024 ids (beyond that, the counting takes
+    // longer than the planning launch it saves), and the LDS of a block stays small
+    const int64_t A = (int64_t)sh.R * sh.TK;
+    return sh.T > 0 && sh.TK <= (int64_t)kRowsPerBlock * kWave && A <= 1024 && sh.E <= 1024;
+}
+
+hipError_t launch_dispatch_small(const Shape& sh, const Tables& tb, const int32_t* ids, const Outputs& out,
+                                 uint32_t* status, const void* x, void* dst, bool direct, int vec, hipStream_t st) {
+    const int64_t N = (int64_t)sh.R * sh.T;
+    const Split sp = make_split(sh.row_bytes, vec, N, sh.num_cu);
+    const int lead = (int)((sh.R + table_blocks(sh.R) + 7) / 8 * 8);
+    const unsigned grid = (unsigned)(lead + piece_blocks(N, sp));
+    const size_t lds = (size_t)small_lds_ints(sh.E, (int64_t)sh.R * sh.TK) * sizeof(int);
+    const PlanArgs a{sh, tb, out, ids, status};
+    return with_vec(vec, [&](auto B) {
+        using V = typename Vec<decltype(B)::value>::T;
+        return with_unroll(sp.cv, [&](auto U) {
+            constexpr int u = decltype(U)::value;
+            if (direct)
+                hipLaunchKernelGGL((dispatch_small_kernel<V, u, true>), dim3(grid), dim3(kBlock), lds, st,
+                                   (const V*)x, (V*)dst, a, sp, lead);
+            else
+                hipLaunchKernelGGL((dispatch_small_kernel<V, u, false>), dim3(grid), dim3(kBlock), lds, st,
+                                   (const V*)x, (V*)dst, a, sp, lead);
+            return hipGetLastError();
+        });
+    });
+}
+
 hipError_t launch_exchange(const Shape& sh, const Tables& tb, const Outputs& out, uint32_t* status, const void* src,
                            void* dst, bool reverse, bool first, int vec, hipStream_t st) {
-    // token order (one piece per token row, the split of pack and combine), or send
-    // order for the bare collective
-    const int64_t rows = first ? (int64_t)sh.R * sh.TK : (int64_t)sh.R * sh.T;
+    const int64_t rows = (int64_t)sh.R * sh.TK;
     const Split sp = make_split(sh.row_bytes, vec, rows, sh.num_cu);
     const unsigned grid = (unsigned)((first ? table_blocks(sh.R) : 0) + piece_blocks(rows, sp));
     if (grid == 0) return hipSuccess;
-    const int64_t bytes = (int64_t)sh.R * sh.TK * sh.row_bytes;
+    const int64_t bytes = rows * sh.row_bytes;
     return with_vec(vec, [&](auto B) {
         using V = typename Vec<decltype(B)::value>::T;
         return with_unroll(sp.cv, [&](auto U) {
@@ -856,14 +1078,14 @@ hipError_t launch_exchange(const Shape& sh, const Tables& tb, const Outputs& out
                 constexpr int u = decltype(U)::value;
                 constexpr bool nt = decltype(NT)::value;
                 if (first)
-                    hipLaunchKernelGGL((alltoallv_kernel<V, u, nt>), dim3(grid), dim3(kBlock), 0, st, (const V*)src,
-                                       (V*)dst, sh, tb, out, status, sp);
+                    hipLaunchKernelGGL((exchange_kernel<V, u, nt, false, true>), dim3(grid), dim3(kBlock), 0, st,
+                                       (const V*)src, (V*)dst, sh, tb, out, status, sp);
                 else if (reverse)
-                    hipLaunchKernelGGL((exchange_kernel<V, u, nt, true>), dim3(grid), dim3(kBlock), 0, st,
-                                       (const V*)src, (V*)dst, sh, tb, sp);
+                    hipLaunchKernelGGL((exchange_kernel<V, u, nt, true, false>), dim3(grid), dim3(kBlock), 0, st,
+                                       (const V*)src, (V*)dst, sh, tb, out, status, sp);
                 else
-                    hipLaunchKernelGGL((exchange_kernel<V, u, nt, false>), dim3(grid), dim3(kBlock), 0, st,
-                                       (const V*)src, (V*)dst, sh, tb, sp);
+                    hipLaunchKernelGGL((exchange_kernel<V, u, nt, false, false>), dim3(grid), dim3(kBlock), 0, st,
+                                       (const V*)src, (V*)dst, sh, tb, out, status, sp);
                 return hipGetLastError();
             });
         });

@@ -135,14 +135,22 @@ def test_repeated_ids_within_a_token_are_sent_k_times(path):
     _full_oracle_check(w, x, ids, gates, path)
 
 
+# Steps of at most 1024 assignments (and at most 256 per rank) dispatch in one launch that
+# places rows by counting over the ids; larger ones plan first.  Cases that probe error
+# handling run on both sides of that line.
+SIDES = [24, 200]
+SIDE_IDS = ["one-launch", "planned"]
+
+
+@pytest.mark.parametrize("tokens", SIDES, ids=SIDE_IDS)
 @pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
-def test_out_of_range_ids_are_dropped_and_flagged(path):
-    w = W.workload("wide", num_ranks=4, tokens_per_rank=24, hidden=128, experts_per_rank=4, top_k=2)
+def test_out_of_range_ids_are_dropped_and_flagged(path, tokens):
+    w = W.workload("wide", num_ranks=4, tokens_per_rank=tokens, hidden=128, experts_per_rank=4, top_k=2)
     x, ids, gates = W.make_inputs(w)
     ids = ids.copy()
     ids[0, 3, 1] = w.num_experts
     ids[2, 0, 0] = -1
-    ids[3, 23, 1] = 1 << 30
+    ids[3, tokens - 1, 1] = 1 << 30
     ref = _full_oracle_check(w, x, ids, gates, path)
     assert ref["status"] == oracle.ST_EXPERT_RANGE
 
