@@ -33,6 +33,7 @@ struct Tables {
     int32_t* eoff;         // [R][E+1]  first place of each expert in the sender's order
     int32_t* xbase;        // [R][E]    expert-major: receive place of (sender, expert)'s first row
     int32_t* recv_eoff;    // [R][epr+1] expert-major: where each local expert's rows start
+    int64_t* dest;         // [R][TK]   direct path: receive row d * cap + q of each (token, slot), -1 none
 };
 
 // Optional copies of the tables for the caller (any may be null).

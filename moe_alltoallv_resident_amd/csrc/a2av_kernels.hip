@@ -433,6 +433,8 @@ __global__ void __launch_bounds__(kBlock) pack_kernel(const V* __restrict__ x, V
     const V* src = x + n * nvec;
     const int32_t* so = tb.send_off + s * (R + 1);
     for (int base = pc.v0; base < pc.v1; base += kWave * U) {
+        // the first piece of a row records where its slots went (for the combine)
+        const bool record = base == 0 && lane == 0;
         V r[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -441,15 +443,20 @@ __global__ void __launch_bounds__(kBlock) pack_kernel(const V* __restrict__ x, V
         }
         for (int j = 0; j < k; ++j) {
             const int pj = __builtin_amdgcn_readlane(my, j);
-            if (pj < 0 || pj >= sh.TK) continue;      // dropped slot (never out of the buffer)
+            if (pj < 0 || pj >= sh.TK) {              // dropped slot (never out of the buffer)
+                if (DIRECT && record) tb.dest[n * k + j] = -1;
+                continue;
+            }
             V* row;
             if constexpr (DIRECT) {
                 const int d = segment_of(so, R, pj, lane);
-                if (d >= R) continue;                   // not a sent row (tables always place it)
-                const int64_t q = sh.layout ? expert_major_place(sh, tb, s, pj, d, lane)
-                                            : recv_base(tb.send_off, R, d, (int)s, lane) + (pj - so[d]);
-                if (q < 0 || q >= sh.cap) continue;     // past the receiver's capacity (flagged)
-                row = dst + ((int64_t)d * sh.cap + q) * nvec;
+                const int64_t q = d >= R ? -1          // not a sent row (tables always place it)
+                                         : sh.layout ? expert_major_place(sh, tb, s, pj, d, lane)
+                                                     : recv_base(tb.send_off, R, d, (int)s, lane) + (pj - so[d]);
+                const int64_t rr = q >= 0 && q < sh.cap ? (int64_t)d * sh.cap + q : -1;   // past capacity: flagged
+                if (record) tb.dest[n * k + j] = rr;
+                if (rr < 0) continue;
+                row = dst + rr * nvec;
             } else {
                 row = dst + (s * sh.TK + pj) * nvec;
             }
@@ -658,6 +665,8 @@ __global__ void __launch_bounds__(kBlock) dispatch_small_kernel(const V* __restr
     for (; j0 + 4 <= k; j0 += 4) place(std::integral_constant<int, 4>{}, j0);
     if (k - j0 >= 2) { place(std::integral_constant<int, 2>{}, j0); j0 += 2; }
     if (k - j0 == 1) place(std::integral_constant<int, 1>{}, j0);
+    // the first piece of a row records where its slots went (for the combine)
+    if (DIRECT && pc.v0 == 0 && lane < k) a.tb.dest[n * k + lane] = my_row;
     for (;;) {
         for (int j = 0; j < k; ++j) {
             const int64_t rj = __shfl(my_row, j, kWave);
@@ -797,19 +806,13 @@ __global__ void __launch_bounds__(kBlock) combine_kernel(const typename Vec<B>::
     const int nvec = sp.nvec;
     const int my_p = lane < k ? tb.pos[n * k + lane] : -1;
     const float my_g = lane < k ? gates[n * k + lane] : 0.0f;
-    // row index of each slot (held by lane j): a send place (staged) or a receive row
-    // (direct); -1 = the slot adds nothing
+    // row index of each slot (held by lane j): a send place (staged) or the receive row
+    // dispatch recorded (direct); -1 = the slot adds nothing
     int64_t my_row = -1;
     if constexpr (DIRECT) {
-        const int32_t* so = tb.send_off + s * (R + 1);
-        for (int j = 0; j < k; ++j) {
-            const int pj = __builtin_amdgcn_readlane(my_p, j);
-            if (pj < 0 || pj >= sh.TK) continue;
-            const int d = segment_of(so, R, pj, lane);
-            if (d >= R) continue;
-            const int64_t q = sh.layout ? expert_major_place(sh, tb, s, pj, d, lane)
-                                        : (int64_t)tb.recv_off[(int64_t)d * (R + 1) + s] + (pj - so[d]);
-            if (lane == j && q >= 0 && q < sh.cap) my_row = (int64_t)d * sh.cap + q;
+        if (lane < k) {
+            const int64_t r = tb.dest[n * k + lane];
+            if (r >= 0 && r < (int64_t)R * sh.cap) my_row = r;
         }
     } else {
         if (my_p >= 0 && my_p < sh.TK) my_row = s * sh.TK + my_p;
