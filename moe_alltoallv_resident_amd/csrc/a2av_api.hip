@@ -240,10 +240,6 @@ int a2av_dispatch(a2av_handle_t h, const void* x, const int32_t* topk_ids, void*
     } else {
         rc = launch_timed(h, kStagePlan, st, [&] { return a2av::launch_plan(sh, tb, topk_ids, out, status, st); });
         if (rc != A2AV_OK) return rc;
-        if (sh.layout == A2AV_LAYOUT_EXPERT_MAJOR) {
-            rc = launch_timed(h, kStagePlan, st, [&] { return a2av::launch_layout(sh, tb, st); });
-            if (rc != A2AV_OK) return rc;
-        }
         rc = launch_timed(h, kStagePack, st,
                           [&] { return a2av::launch_pack(sh, tb, out, status, x, dst, h->direct, vec, st); });
         if (rc != A2AV_OK) return rc;

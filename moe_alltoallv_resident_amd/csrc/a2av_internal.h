@@ -52,8 +52,6 @@ int plan_waves(int32_t E);
 
 hipError_t launch_plan(const Shape& sh, const Tables& tb, const int32_t* ids, const Outputs& out,
                        uint32_t* status, hipStream_t st);
-// Expert-major receive places (one wavefront per receiver); after planning.
-hipError_t launch_layout(const Shape& sh, const Tables& tb, hipStream_t st);
 hipError_t launch_plan_from_counts(const Shape& sh, const Tables& tb, const int32_t* send_counts,
                                    uint32_t* status, hipStream_t st);
 // Small steps (decode sizes): planning, receiver tables (and expert-major places) and
@@ -62,7 +60,8 @@ bool small_dispatch(const Shape& sh);
 hipError_t launch_dispatch_small(const Shape& sh, const Tables& tb, const int32_t* ids, const Outputs& out,
                                  uint32_t* status, const void* x, void* dst, bool direct, int vec, hipStream_t st);
 // pack: staged (dst = send buffer) or direct (dst = receive buffer); also builds the
-// receive tables (and the caller's copies in `out`).
+// receive tables (and the caller's copies in `out`) and, for expert-major buffers, the
+// expert-major places.
 hipError_t launch_pack(const Shape& sh, const Tables& tb, const Outputs& out, uint32_t* status, const void* x,
                        void* dst, bool direct, int vec, hipStream_t st);
 // exchange: forward (send -> recv) or reverse (recv layout -> send places); `first`

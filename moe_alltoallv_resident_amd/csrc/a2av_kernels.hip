@@ -278,11 +278,9 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanArgs a) {
 // in that order: an exclusive scan over d's epr x R pairs.  One wavefront per receiver;
 // lane l takes pair c0 + l of each run of 64, the run's counts are loaded together (the
 // next run's while this one is scanned), and a wavefront scan with a carry between runs
-// gives xbase[s][e] and, at each expert's first sender, recv_eoff[d][le].
-__global__ void __launch_bounds__(kBlock) layout_kernel(Shape sh, Tables tb) {
-    const int lane = lane_id();
-    const int d = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
-    if (d >= sh.R) return;
+// gives xbase[s][e] and, at each expert's first sender, recv_eoff[d][le].  Run by the
+// receiver-table wavefronts of pack, so the tables are there for every later kernel.
+__device__ void write_expert_major_tables(const Shape& sh, const Tables& tb, int d, int lane) {
     const int R = sh.R, E = sh.E, epr = sh.epr;
     const int pairs = epr * R;   // = E
     auto load = [&](int i) -> int {
@@ -325,6 +323,24 @@ __device__ __forceinline__ int64_t expert_major_place(const Shape& sh, const Tab
                                                       int lane) {
     const int e = expert_of(sh, tb, s, p, d, lane);
     return (int64_t)tb.xbase[s * sh.E + e] + (p - tb.eoff[s * (sh.E + 1) + e]);
+}
+
+// The same place computed from the plan's counts alone (for the kernel that runs
+// beside the table writers): d's rows for its experts below e over all senders, plus
+// e's rows from the senders before s, plus p's rank in s's run of e; the first two are
+// summed over d's (local expert, sender) pairs, one pair per lane at a time.
+__device__ __forceinline__ int64_t expert_major_place_counted(const Shape& sh, const Tables& tb, int64_t s,
+                                                              int64_t p, int d, int lane) {
+    const int e = expert_of(sh, tb, s, p, d, lane);
+    const int R = sh.R, E = sh.E, epr = sh.epr, le = e - d * epr;
+    const int pairs = epr * R;
+    int acc = 0;
+    for (int c0 = 0; c0 < pairs; c0 += kWave) {
+        const int i = c0 + lane;
+        const int l2 = i / R, s2 = i - l2 * R;
+        if (i < pairs && (l2 < le || (l2 == le && s2 < s))) acc += tb.cnt[(int64_t)s2 * E + d * epr + l2];
+    }
+    return (int64_t)wave_sum(acc) + (p - tb.eoff[s * (E + 1) + e]);
 }
 
 // The bare collective's planning: send offsets from caller counts, one block per sender.
@@ -419,7 +435,10 @@ __global__ void __launch_bounds__(kBlock) pack_kernel(const V* __restrict__ x, V
     const int64_t rblk = ((int64_t)sh.R * sh.T * sp.cpr + kRowsPerBlock - 1) / kRowsPerBlock;
     if ((int64_t)blockIdx.x >= rblk) {
         const int64_t d = ((int64_t)blockIdx.x - rblk) * kRowsPerBlock + threadIdx.x / kWave;
-        if (d < sh.R) write_recv_tables(sh, tb, out, status, (int)d, lane);
+        if (d < sh.R) {
+            write_recv_tables(sh, tb, out, status, (int)d, lane);
+            if (sh.layout) write_expert_major_tables(sh, tb, (int)d, lane);
+        }
         return;
     }
     const Piece pc = piece_of((int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kWave, sp);
@@ -451,7 +470,7 @@ __global__ void __launch_bounds__(kBlock) pack_kernel(const V* __restrict__ x, V
             if constexpr (DIRECT) {
                 const int d = segment_of(so, R, pj, lane);
                 const int64_t q = d >= R ? -1          // not a sent row (tables always place it)
-                                         : sh.layout ? expert_major_place(sh, tb, s, pj, d, lane)
+                                         : sh.layout ? expert_major_place_counted(sh, tb, s, pj, d, lane)
                                                      : recv_base(tb.send_off, R, d, (int)s, lane) + (pj - so[d]);
                 const int64_t rr = q >= 0 && q < sh.cap ? (int64_t)d * sh.cap + q : -1;   // past capacity: flagged
                 if (record) tb.dest[n * k + j] = rr;
@@ -537,7 +556,8 @@ __device__ __forceinline__ void count_places(const Shape& sh, const int* sids, i
 // (epr x R ints of LDS, zeroed by the caller): hist[le * R + s] = rows sender s sends to
 // d's local expert le, by LDS atomic increments.  count_tables_write then forms
 // recv_counts / recv_off as write_recv_tables does and, for expert-major buffers, xbase
-// and recv_eoff as layout_kernel does; the caller puts a block barrier between the two.
+// and recv_eoff as write_expert_major_tables does; the caller puts a block barrier
+// between the two.
 __device__ __forceinline__ void count_tables_fill(const Shape& sh, const int* sids, int d, int lane, int* hist) {
     const int A = sh.R * (int)sh.TK, TK = (int)sh.TK;
     const int elo = d * sh.epr;
@@ -1000,10 +1020,6 @@ hipError_t launch_plan(const Shape& sh, const Tables& tb, const int32_t* ids, co
     return hipGetLastError();
 }
 
-hipError_t launch_layout(const Shape& sh, const Tables& tb, hipStream_t st) {
-    hipLaunchKernelGGL(layout_kernel, dim3((unsigned)table_blocks(sh.R)), dim3(kBlock), 0, st, sh, tb);
-    return hipGetLastError();
-}
 
 hipError_t launch_plan_from_counts(const Shape& sh, const Tables& tb, const int32_t* send_counts, uint32_t* status,
                                    hipStream_t st) {
