@@ -67,15 +67,17 @@ def step_bytes(w, direct):
     return (2 * (N + A) if direct else 2 * N + 6 * A) * row
 
 
-def stage_bytes(w):
-    """Algorithmic bytes per launch of each stage (real rows only)."""
+def stage_bytes(w, direct):
+    """Algorithmic bytes per launch of each stage (real rows only).  Index bytes: pack
+    reads each assignment's place (4 B) and, on the direct path, records its receive row
+    (8 B); the combine reads each gate (4 B) and the place (4 B) or receive row (8 B)."""
     N, A, row = w.tokens, w.assignments, w.row_bytes
     return {
         "plan": A * 4 + 4 * (w.num_ranks * w.num_experts + w.num_ranks * (w.num_ranks + 1)) + A * 4,
-        "pack": (N + A) * row + A * 4,
+        "pack": (N + A) * row + A * (12 if direct else 4),
         "exchange": 2 * A * row,
         "return": 2 * A * row,
-        "combine": (A + N) * row + A * 8,
+        "combine": (A + N) * row + A * (12 if direct else 8),
     }
 
 
@@ -241,7 +243,7 @@ def time_path(torch, a2av, w, xt, idt, gt, name, steps, warmup):
     dc_ms = sum(stage_ms.values())
     nbytes = step_bytes(w, direct)
     gbps = nbytes / (dc_ms * 1e-3) / 1e9
-    sb = stage_bytes(w)
+    sb = stage_bytes(w, direct)
     dom = max((n for n in launch_ms if n != "plan"), key=lambda n: launch_ms[n])
     dom_gbps = sb[dom] / (launch_ms[dom] * 1e-3) / 1e9
     log(f"{path}: stages (us/launch): " + ", ".join(f"{n} {v * 1e3:.1f}" for n, v in stage_ms.items()))
