@@ -8,10 +8,13 @@ rank), top-1 with Zipf(1.2) expert popularity.
 
 Printed: ONE JSON line.  `value` is the effective HBM bandwidth of dispatch+combine, the
 algorithmic bytes of the staged path ((2N + 6A) rows of real tokens) divided by the
-dispatch+combine time from HIP events recorded between the library's kernels on the
-stream they run on; `us_per_step` is that time; `ms_per_step` is the wall time of a
-whole step (expert stand-in included) between two synchronisations.  `roofline` is for
-the slowest kernel of the step; `cpu_baseline` is the CPU oracle on a bounded sample of
+dispatch+combine time per step; `us_per_step` is that time: the median over 5 trials of
+K back-to-back dispatch+combine pairs / K, with events only around each loop, so launch
+gaps count and no event sits between kernels
+(`us_per_step_min` is the fastest trial, `us_per_step_kernels` the sum of the library's
+per-kernel event times, `stage_us` their breakdown); `ms_per_step` is a whole step
+(expert stand-in included).  `roofline` is for the slowest kernel of the step, from its
+per-kernel event time; `cpu_baseline` is the CPU oracle on a bounded sample of
 the same workload; `decode_graph` and `edge_graph` are the decode and edge shapes
 captured in hipGraphs and replayed with routing that changes on the device each step.
 """
@@ -163,11 +166,13 @@ def main():
         "value": head["GBps"],
         "unit": "GB/s",
         "us_per_step": head["us_per_step"],
+        "us_per_step_min": head["us_per_step_min"],
+        "us_per_step_kernels": head["us_per_step_kernels"],
         "pct_hbm_peak": head["pct_hbm_peak"],
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": head["ms_per_step_wall"],
+        "ms_per_step": head["ms_per_step_full"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -185,7 +190,8 @@ def main():
                          frac_of_row_copy=round(head["roofline"]["achieved"] / row_copy_gbps, 4)),
     }
     for p in paths[1:]:
-        result[f"{p.replace('-', '_')}_path"] = {k: v for k, v in measured[p].items() if k != "ms_per_step_wall"}
+        result[f"{p.replace('-', '_')}_path"] = {k: v for k, v in measured[p].items()
+                                                 if k not in ("ms_per_step_wall", "ms_per_step_full")}
     del xt
     torch.cuda.empty_cache()
 
@@ -206,9 +212,13 @@ def path_config(a2av, name):
     return path, layout
 
 
-def time_path(torch, a2av, w, xt, idt, gt, name, steps, warmup):
-    """Warm-up, then `steps` timed steps of one path with HIP events recorded between the
-    library's kernels (on the stream they run on) and the wall clock around them."""
+def time_path(torch, a2av, w, xt, idt, gt, name, steps, warmup, trials=5):
+    """One path: warm-up; `steps` steps with HIP events recorded between the library's
+    kernels (on the stream they run on) for the per-kernel breakdown and the roofline;
+    then `trials` end-to-end runs with events only around the whole loop: `steps`
+    dispatch+combine pairs (the headline: median trial, launch gaps included, no event
+    between kernels; the minimum beside it), and `steps` full steps with the expert
+    stand-in between them."""
     path_id, layout = path_config(a2av, name)
     direct = path_id == a2av.PATH_DIRECT
     path = name
@@ -220,6 +230,19 @@ def time_path(torch, a2av, w, xt, idt, gt, name, steps, warmup):
         s.dispatch(xt, idt)
         s.expert(s.recv, s.recv, w.expert_mode)
         s.combine(s.recv, gt, y)
+
+    def dispatch_combine():
+        s.dispatch(xt, idt)
+        s.combine(s.recv, gt, y)
+
+    def loop_ms(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
 
     log(f"{path}: warmup {warmup}")
     for _ in range(warmup):
@@ -234,26 +257,36 @@ def time_path(torch, a2av, w, xt, idt, gt, name, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_sum, launches = a2av.a2av_timing_end(s.handle)
+    full_ms, dc_trials = [], []
+    for _ in range(trials):
+        full_ms.append(loop_ms(step))
+        dc_trials.append(loop_ms(dispatch_combine))
     status = int(s.status.item())
     if status != 0:
         raise RuntimeError(f"device status {status} during the benchmark")
+    full_ms.sort()
+    dc_trials.sort()
+    dc_ms = dc_trials[len(dc_trials) // 2]
     # per step (a stage may launch more than one kernel), and per launch
     stage_ms = {n: ms_sum[i] / steps for i, n in enumerate(a2av.STAGE_NAMES) if launches[i]}
     launch_ms = {n: ms_sum[i] / launches[i] for i, n in enumerate(a2av.STAGE_NAMES) if launches[i]}
-    dc_ms = sum(stage_ms.values())
     nbytes = step_bytes(w, direct)
     gbps = nbytes / (dc_ms * 1e-3) / 1e9
     sb = stage_bytes(w, direct)
     dom = max((n for n in launch_ms if n != "plan"), key=lambda n: launch_ms[n])
     dom_gbps = sb[dom] / (launch_ms[dom] * 1e-3) / 1e9
-    log(f"{path}: stages (us/launch): " + ", ".join(f"{n} {v * 1e3:.1f}" for n, v in stage_ms.items()))
+    log(f"{path}: dispatch+combine {dc_ms * 1e3:.1f} us per step (median of {trials}); stages (us/launch): "
+        + ", ".join(f"{n} {v * 1e3:.1f}" for n, v in stage_ms.items()))
     s.close()
     del y, s
     torch.cuda.empty_cache()
     return {
         "GBps": round(gbps, 1),
         "us_per_step": round(dc_ms * 1e3, 2),
+        "us_per_step_min": round(dc_trials[0] * 1e3, 2),
+        "us_per_step_kernels": round(sum(stage_ms.values()) * 1e3, 2),
         "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+        "ms_per_step_full": round(full_ms[len(full_ms) // 2], 4),
         "ms_per_step_wall": round(wall / steps * 1e3, 4),
         "bytes_per_step": nbytes,
         "stage_us": {n: round(v * 1e3, 2) for n, v in stage_ms.items()},

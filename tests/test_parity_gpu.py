@@ -84,6 +84,11 @@ SMALL = [
     ("edge", dict(num_ranks=1024, tokens_per_rank=2, hidden=16, routing="uniform")),
     # long runs per wavefront: 8192 assignments per rank spread over 16 wavefronts
     ("decode", dict(num_ranks=2, tokens_per_rank=8192, hidden=8)),
+    # one-launch dispatch: slots placed in groups of 4, 2 and 1 (k = 7)
+    ("wide", dict(num_ranks=16, tokens_per_rank=8, hidden=64, experts_per_rank=4, top_k=7)),
+    # one-launch dispatch at its limits (256 assignments per rank, 1024 in all), and just past
+    ("decode", dict(num_ranks=4, tokens_per_rank=256, hidden=256)),
+    ("decode", dict(num_ranks=4, tokens_per_rank=257, hidden=256)),
     # a small receive capacity (rows dropped, flagged, counts kept)
     ("wide", dict(num_ranks=4, tokens_per_rank=30, hidden=64, experts_per_rank=2, top_k=2,
                   recv_capacity_rows=20)),
