@@ -141,7 +141,10 @@ int64_t a2av_workspace_bytes(const a2av_config_t* cfg);
  *   4. exchange: every segment copied into the receiving rank's slice of recv at the
  *      offset the device tables give.
  * The direct path fuses 3 and 4: each row goes from x straight to its receive place
- * (the pages' zero-copy transfer, user buffer to peer user buffer).
+ * (the pages' zero-copy transfer, user buffer to peer user buffer).  Steps of at most
+ * 1024 assignments (256 per rank) and 1024 experts run 1-3 as a single launch: every
+ * row finds its place by counting, over topk_ids, the assignments before it in its
+ * destination's order (the same place the scans give).  The results are identical.
  * x (device) [R][T][H] dtype; topk_ids (device) [R][T][k].  recv (device, caller
  * owned) [R][cap][H]: only the first min(recv_offsets[d][R], cap) rows of slice d are
  * written.  split, recv_counts, recv_offsets (device, optional: NULL = not wanted)
