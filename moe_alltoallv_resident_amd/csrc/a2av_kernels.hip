@@ -18,7 +18,10 @@
 // Everything but planning is a row copy or gather bound by HBM bandwidth: rows move as
 // 16-byte vectors, one 64-lane wavefront per row, with all of a row's loads issued
 // before its stores, non-temporal for buffers too large to stay in cache.  Nothing here
-// is a dense contraction, so no matrix-core instruction is used.
+// is a dense contraction, so no matrix-core instruction is used.  Small steps (decode
+// sizes) are bound by launches and dependent table reads instead of bytes; there plan,
+// tables and pack run as one launch in which every block works from the routing ids
+// (dispatch_small_kernel).
 #include "a2av_internal.h"
 
 #include <algorithm>
@@ -809,7 +812,7 @@ template <int B, int DT> struct Elems {
 // combine: y[s][t] = round(sum_j g_j * row_j) with one float32 FMA per slot in slot
 // order, starting from 0.  row_j is the returned row at send place pos_j (staged) or
 // the expert output in the receiver's buffer (direct).
-template <int B, int DT, int U, bool NT, bool DIRECT>
+template <int B, int DT, int U, bool NT, bool DIRECT, bool PAIRS>
 __global__ void __launch_bounds__(kBlock) combine_kernel(const typename Vec<B>::T* __restrict__ rows,
                                                          const float* __restrict__ gates,
                                                          typename Vec<B>::T* __restrict__ y, Shape sh, Tables tb,
@@ -844,21 +847,48 @@ __global__ void __launch_bounds__(kBlock) combine_kernel(const typename Vec<B>::
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int e = 0; e < NE; ++e) acc[u][e] = 0.0f;
-        for (int j = 0; j < k; ++j) {
+        // PAIRS (k > 1): slots in pairs, each slot's loads issued before the previous
+        // slot's multiply-adds so that a wavefront always has rows in flight; the adds
+        // stay in slot order
+        auto slot_row = [&](int j) -> const V* {   // null: no slot, or a dropped one
+            if (j >= k) return nullptr;
             const int64_t rj = __shfl(my_row, j, kWave);
-            const float gj = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_g), j));
-            if (rj < 0) continue;                      // dropped slot adds nothing
-            const V* row = rows + rj * nvec;
-            V r[U];
+            return rj < 0 ? nullptr : rows + rj * nvec;
+        };
+        auto load = [&](V* r, const V* row) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int v = base + u * kWave + lane;
                 if (v < pc.v1) r[u] = ld<NT>(row + v);
             }
+        };
+        auto add = [&](const V* r, int j) {
+            const float gj = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_g), j));
 #pragma unroll
             for (int u = 0; u < U; ++u)
 #pragma unroll
                 for (int e = 0; e < NE; ++e) acc[u][e] = __builtin_fmaf(gj, El::get(r[u], e), acc[u][e]);
+        };
+        if constexpr (PAIRS) {
+            V ra[U], rb[U];
+            const V* pa = slot_row(0);
+            if (pa) load(ra, pa);
+            for (int j = 0; j < k; j += 2) {
+                const V* pb = slot_row(j + 1);
+                if (pb) load(rb, pb);
+                if (pa) add(ra, j);
+                pa = slot_row(j + 2);
+                if (pa) load(ra, pa);
+                if (pb) add(rb, j + 1);
+            }
+        } else {
+            for (int j = 0; j < k; ++j) {
+                const V* p = slot_row(j);
+                if (!p) continue;
+                V r[U];
+                load(r, p);
+                add(r, j);
+            }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -1120,16 +1150,27 @@ static hipError_t launch_combine_t(const Shape& sh, const Tables& tb, const void
     const int64_t bytes = N * sh.row_bytes;
     return with_unroll(sp.cv, [&](auto U) {
         return with_nt(bytes, [&](auto NT) {
-            // keep float accumulators within a sane register budget
-            constexpr int UU = (decltype(U)::value * Elems<B, DT>::N > 64) ? 64 / Elems<B, DT>::N
-                                                                            : decltype(U)::value;
+            // keep float accumulators and the two slots' rows within a sane register
+            // budget: 64 accumulators for one slot, 32 when slots are double-buffered
+            constexpr int NE = Elems<B, DT>::N, U0 = decltype(U)::value;
+            constexpr int U1 = U0 * NE > 64 ? 64 / NE : U0, UK = U0 * NE > 32 ? 32 / NE : U0;
             constexpr bool nt = decltype(NT)::value;
-            if (direct)
-                hipLaunchKernelGGL((combine_kernel<B, DT, UU, nt, true>), dim3(piece_blocks(N, sp)), dim3(kBlock), 0,
-                                   st, (const V*)rows, gates, (V*)y, sh, tb, sp);
-            else
-                hipLaunchKernelGGL((combine_kernel<B, DT, UU, nt, false>), dim3(piece_blocks(N, sp)), dim3(kBlock), 0,
-                                   st, (const V*)rows, gates, (V*)y, sh, tb, sp);
+            const unsigned grid = piece_blocks(N, sp);
+            if (sh.k == 1) {
+                if (direct)
+                    hipLaunchKernelGGL((combine_kernel<B, DT, U1, nt, true, false>), dim3(grid), dim3(kBlock), 0, st,
+                                       (const V*)rows, gates, (V*)y, sh, tb, sp);
+                else
+                    hipLaunchKernelGGL((combine_kernel<B, DT, U1, nt, false, false>), dim3(grid), dim3(kBlock), 0, st,
+                                       (const V*)rows, gates, (V*)y, sh, tb, sp);
+            } else {
+                if (direct)
+                    hipLaunchKernelGGL((combine_kernel<B, DT, UK, nt, true, true>), dim3(grid), dim3(kBlock), 0, st,
+                                       (const V*)rows, gates, (V*)y, sh, tb, sp);
+                else
+                    hipLaunchKernelGGL((combine_kernel<B, DT, UK, nt, false, true>), dim3(grid), dim3(kBlock), 0, st,
+                                       (const V*)rows, gates, (V*)y, sh, tb, sp);
+            }
             return hipGetLastError();
         });
     });
