@@ -1,0 +1,107 @@
+"""Host-side logic of bench.py (no GPU): the algorithmic byte counts every bandwidth
+figure divides by, the one-GPU guard, and the profile summaries read from rocprofv3
+databases."""
+import os
+import sqlite3
+import subprocess
+import sys
+
+import pytest
+
+import bench
+from moe_alltoallv_resident_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# (2N + 6A) rows staged and 2(N + A) rows direct, N = R*T tokens, A = N*k assignments,
+# worked out by hand from each workload's shape
+BYTES = {
+    # name: (N, A, row bytes)
+    "tiny": (256, 512, 512),
+    "decode": (1024, 1024, 10240),
+    "prefill": (65536, 65536, 10240),
+    "wide": (32768, 262144, 14336),
+    "edge": (1024, 2048, 4096),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BYTES))
+def test_step_bytes_are_the_real_rows_moved(name):
+    N, A, row = BYTES[name]
+    w = W.workload(name)
+    assert (w.tokens, w.assignments, w.row_bytes) == (N, A, row)
+    assert bench.step_bytes(w, False) == (2 * N + 6 * A) * row
+    assert bench.step_bytes(w, True) == 2 * (N + A) * row
+
+
+def test_step_bytes_at_the_prefill_and_wide_shapes():
+    # the figures quoted next to the measurements: 5.369 GB / 2.684 GB at prefill,
+    # 23.488 GB / 8.456 GB at the wide shape
+    assert bench.step_bytes(W.workload("prefill"), False) == 5_368_709_120
+    assert bench.step_bytes(W.workload("prefill"), True) == 2_684_354_560
+    assert bench.step_bytes(W.workload("wide"), False) == 23_488_102_400
+    assert bench.step_bytes(W.workload("wide"), True) == 8_455_716_864
+
+
+def test_stage_bytes_sum_to_the_step_rows():
+    for name in BYTES:
+        w = W.workload(name)
+        N, A, row = BYTES[name]
+        staged = bench.stage_bytes(w, False)
+        rows = staged["pack"] + staged["exchange"] + staged["return"] + staged["combine"]
+        assert rows - A * (4 + 8) == bench.step_bytes(w, False)
+        direct = bench.stage_bytes(w, True)
+        assert direct["pack"] + direct["combine"] - A * (12 + 12) == bench.step_bytes(w, True)
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def _fake_db(path):
+    c = sqlite3.connect(path)
+    c.execute("create table kernels (name text, grid_x int, workgroup_x int, duration int)")
+    c.executemany("insert into kernels values (?, ?, ?, ?)", [
+        ("void a2av::(anonymous namespace)::pack_kernel<unsigned int __vector(4), 16, true, false>(int)",
+         4194816, 256, 240000),
+        ("void a2av::(anonymous namespace)::pack_kernel<unsigned int __vector(4), 16, true, false>(int)",
+         4194816, 256, 260000),
+        ("void a2av::(anonymous namespace)::plan_kernel<8>(int)", 8192, 1024, 12000),
+    ])
+    c.execute("create table counters_collection (kernel_name text, grid_size_x int, counter_name text, value real)")
+    c.executemany("insert into counters_collection values (?, ?, ?, ?)", [
+        ("void a2av::(anonymous namespace)::pack_kernel<unsigned int __vector(4), 16, true, false>(int)",
+         4194816, "FETCH_SIZE", 100.0),
+        ("void a2av::(anonymous namespace)::pack_kernel<unsigned int __vector(4), 16, true, false>(int)",
+         4194816, "FETCH_SIZE", 300.0),
+    ])
+    c.execute("create table regions (category text, name text)")
+    c.executemany("insert into regions values (?, ?)", [("HIP_RUNTIME_API", "hipGraphLaunch")] * 3 +
+                  [("HIP_RUNTIME_API", "hipGetDevice")] * 2 + [("MARKER", "other")])
+    c.commit()
+    c.close()
+
+
+def test_profile_summary_averages_durations_and_counters(tmp_path, capsys):
+    db = str(tmp_path / "k_results.db")
+    _fake_db(db)
+    bench.profile_summary([db])
+    out = capsys.readouterr().out
+    pack = next(ln for ln in out.splitlines() if ln.startswith("| pack_kernel<u32x4, 16, true, false>"))
+    cells = [c.strip() for c in pack.strip("|").split("|")]
+    # kernel, grid, block, launches, avg, min, max (us), avg FETCH_SIZE
+    assert cells[1:] == ["4194816", "256", "2", "250.00", "240.00", "260.00", "200.0"]
+    assert any(ln.startswith("| plan_kernel<8> | 8192 | 1024 | 1 | 12.00") for ln in out.splitlines())
+
+
+def test_api_summary_counts_hip_calls_only(tmp_path, capsys):
+    db = str(tmp_path / "a_results.db")
+    _fake_db(db)
+    bench.api_summary([db])
+    out = capsys.readouterr().out
+    assert "| hipGraphLaunch | 3 |" in out and "| hipGetDevice | 2 |" in out
+    assert "other" not in out
