@@ -142,7 +142,7 @@ int64_t a2av_workspace_bytes(const a2av_config_t* cfg);
  *      offset the device tables give.
  * The direct path fuses 3 and 4: each row goes from x straight to its receive place
  * (the pages' zero-copy transfer, user buffer to peer user buffer).  Steps of at most
- * 1024 assignments (256 per rank) and 1024 experts run 1-3 as a single launch: every
+ * 2048 assignments (256 per rank) and 1024 experts run 1-3 as a single launch: every
  * row finds its place by counting, over topk_ids, the assignments before it in its
  * destination's order (the same place the scans give).  The results are identical.
  * x (device) [R][T][H] dtype; topk_ids (device) [R][T][k].  recv (device, caller

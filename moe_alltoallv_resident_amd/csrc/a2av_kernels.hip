@@ -519,14 +519,19 @@ __device__ __forceinline__ void stage_ids(const int32_t* __restrict__ ids, int64
 // s's rows for d's experts below e, then s's earlier rows for e.  Direct, expert-major:
 // d's rows for its experts below e, then the earlier rows for e over all senders in
 // (sender, token, slot) order.
+// `part` of `parts` equal slices of the scanned ids is counted (the caller adds the
+// parts up).
 template <bool DIRECT, int NS>
 __device__ __forceinline__ void count_places(const Shape& sh, const int* sids, int s, int me0, const int* e,
-                                             const int* d, int* q, int lane) {
+                                             const int* d, int* q, int lane, int part, int parts) {
     const int A = sh.R * (int)sh.TK, TK = (int)sh.TK;
     int lo, hi, before;       // ids scanned, and the index below which every row of d counts
     if (!DIRECT) { lo = s * TK; hi = lo + TK; before = lo; }
     else if (sh.layout) { lo = 0; hi = A; before = 0; }
     else { lo = 0; hi = (s + 1) * TK; before = s * TK; }
+    const int slice = (hi - lo + parts - 1) / parts;
+    lo += part * slice;
+    hi = min(hi, lo + slice);
     int elo[NS], ehi[NS];
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
@@ -557,10 +562,11 @@ __device__ __forceinline__ void count_places(const Shape& sh, const int* sids, i
 
 // Receiver d's tables counted from the ids (in LDS) by one wavefront into `hist`
 // (epr x R ints of LDS, zeroed by the caller): hist[le * R + s] = rows sender s sends to
-// d's local expert le, by LDS atomic increments.  count_tables_write then forms
-// recv_counts / recv_off as write_recv_tables does and, for expert-major buffers, xbase
-// and recv_eoff as write_expert_major_tables does; the caller puts a block barrier
-// between the two.
+// d's local expert le, by LDS atomic increments (independent of one another, so they
+// pipeline; a loop that waits on LDS every step is slow here, where the row
+// wavefronts keep the LDS busy).  count_tables_write then forms recv_counts / recv_off
+// as write_recv_tables does and, for expert-major buffers, xbase and recv_eoff as
+// write_expert_major_tables does; the caller puts a block barrier between the two.
 __device__ __forceinline__ void count_tables_fill(const Shape& sh, const int* sids, int d, int lane, int* hist) {
     const int A = sh.R * (int)sh.TK, TK = (int)sh.TK;
     const int elo = d * sh.epr;
@@ -614,10 +620,13 @@ __device__ void count_tables_write(const Shape& sh, const Tables& tb, const Outp
 }
 
 // LDS (ints) of the one-launch dispatch: planning needs 5 rows of E counters, a table
-// block 4 histograms of E plus the ids, a row block the ids.
+// block 4 histograms of E plus the ids, a row block the ids and its wavefronts' partial
+// counts (4 x 64).
 __host__ __device__ __forceinline__ int64_t small_lds_ints(int64_t E, int64_t A) {
     const int64_t plan = (kRowsPerBlock + 1) * E, tables = kRowsPerBlock * E + A;
-    return plan > tables ? plan : tables;
+    const int64_t rows = A + kRowsPerBlock * kMaxTopK;
+    const int64_t m = plan > tables ? plan : tables;
+    return m > rows ? m : rows;
 }
 
 template <typename V, int U, bool DIRECT>
@@ -650,6 +659,11 @@ __global__ void __launch_bounds__(kBlock) dispatch_small_kernel(const V* __restr
     const bool live = n < (int64_t)R * sh.T;
     const int64_t s = n / sh.T;
     const int k = sh.k, nvec = sp.nvec;
+    // when a row is cut into a multiple of 4 pieces, a block's 4 wavefronts hold pieces
+    // of the same row and each counts a quarter of the ids
+    const bool coop = sp.cpr % kRowsPerBlock == 0;
+    const int part = coop ? w : 0, parts = coop ? kRowsPerBlock : 1;
+    int* partial = lds + A;                         // [4][kMaxTopK] per-wavefront counts
     const V* src = x + n * nvec;
     V r[U];
     int base = pc.v0;
@@ -662,32 +676,46 @@ __global__ void __launch_bounds__(kBlock) dispatch_small_kernel(const V* __restr
     }
     stage_ids(a.ids, A, lds);
     __syncthreads();
-    if (!live) return;
-    // lane j: slot j's destination row, -1 if the slot has none
-    int64_t my_row = -1;
+    if (!live) return;                              // uniform over the block when coop
+    // slot j's expert and destination (lane j), and its count (lane 0 of each
+    // wavefront records the part it counted)
+    const int my_v = lane < k ? lds[n * k + lane] : -1;
+    const int my_e = my_v >= 0 && my_v < sh.E ? my_v : -1;   // out of range: dropped (planning flags it)
+    const int my_d = my_e >= 0 ? my_e / sh.epr : 0;
+    int my_q = 0;
     auto place = [&](auto NSC, int j0) {
         constexpr int NS = decltype(NSC)::value;
         int e[NS], d[NS], q[NS];
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
-            const int v = lds[n * k + j0 + j];
-            e[j] = v >= 0 && v < sh.E ? v : -1;     // out-of-range id: dropped (planning flags it)
-            d[j] = e[j] >= 0 ? e[j] / sh.epr : 0;
+            e[j] = __builtin_amdgcn_readlane(my_e, j0 + j);
+            d[j] = __builtin_amdgcn_readlane(my_d, j0 + j);
         }
-        count_places<DIRECT, NS>(sh, lds, (int)s, (int)(n * k + j0), e, d, q, lane);
+        count_places<DIRECT, NS>(sh, lds, (int)s, (int)(n * k + j0), e, d, q, lane, part, parts);
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
-            if (e[j] < 0) continue;
-            int64_t row;
-            if constexpr (DIRECT) row = q[j] < sh.cap ? (int64_t)d[j] * sh.cap + q[j] : -1;   // past capacity
-            else row = s * sh.TK + q[j];
-            if (lane == j0 + j) my_row = row;
+            if (coop && lane == 0) partial[w * kMaxTopK + j0 + j] = q[j];
+            if (lane == j0 + j) my_q = q[j];
         }
     };
     int j0 = 0;
     for (; j0 + 4 <= k; j0 += 4) place(std::integral_constant<int, 4>{}, j0);
     if (k - j0 >= 2) { place(std::integral_constant<int, 2>{}, j0); j0 += 2; }
     if (k - j0 == 1) place(std::integral_constant<int, 1>{}, j0);
+    if (coop) {
+        __syncthreads();
+        if (lane < k) {
+            my_q = 0;
+#pragma unroll
+            for (int p = 0; p < kRowsPerBlock; ++p) my_q += partial[p * kMaxTopK + lane];
+        }
+    }
+    // lane j: slot j's destination row, -1 if the slot has none
+    int64_t my_row = -1;
+    if (lane < k && my_e >= 0) {
+        if constexpr (DIRECT) my_row = my_q < sh.cap ? (int64_t)my_d * sh.cap + my_q : -1;   // past capacity
+        else my_row = s * sh.TK + my_q;
+    }
     // the first piece of a row records where its slots went (for the combine)
     if (DIRECT && pc.v0 == 0 && lane < k) a.tb.dest[n * k + lane] = my_row;
     for (;;) {
@@ -1083,11 +1111,12 @@ hipError_t launch_pack(const Shape& sh, const Tables& tb, const Outputs& out, ui
 }
 
 bool small_dispatch(const Shape& sh) {
-    // planning fits one 64-assignment batch per wavefront of a 4-wavefront block, each
-    // row wavefront counts over at most 1024 ids (beyond that, the counting takes
-    // longer than the planning launch it saves), and the LDS of a block stays small
+    // planning fits one 64-assignment batch per wavefront of a 4-wavefront block, the
+    // ids fit LDS beside the counters, at most 2048 ids are counted per row (beyond
+    // that, the counting takes longer than the planning launch it saves) and the LDS
+    // of a block stays small
     const int64_t A = (int64_t)sh.R * sh.TK;
-    return sh.T > 0 && sh.TK <= (int64_t)kRowsPerBlock * kWave && A <= 1024 && sh.E <= 1024;
+    return sh.T > 0 && sh.TK <= (int64_t)kRowsPerBlock * kWave && A <= 2048 && sh.E <= 1024;
 }
 
 hipError_t launch_dispatch_small(const Shape& sh, const Tables& tb, const int32_t* ids, const Outputs& out,

@@ -62,8 +62,8 @@ def test_host_side_rejections_enqueue_nothing():
             a2av.a2av_create(bad)
 
 
-# 64 tokens per rank: one-launch dispatch (512 assignments); 200: planned (1600)
-@pytest.mark.parametrize("tokens", [64, 200], ids=["one-launch", "planned"])
+# 64 tokens per rank: one-launch dispatch (512 assignments); 300: planned (2400)
+@pytest.mark.parametrize("tokens", [64, 300], ids=["one-launch", "planned"])
 @pytest.mark.parametrize("layout", [a2av.LAYOUT_SOURCE_MAJOR, a2av.LAYOUT_EXPERT_MAJOR], ids=["srcmaj", "expmaj"])
 @pytest.mark.parametrize("path", [a2av.PATH_STAGED, a2av.PATH_DIRECT], ids=["staged", "direct"])
 def test_receive_overflow_keeps_guard_rows_and_true_counts(path, layout, tokens):

@@ -86,9 +86,11 @@ SMALL = [
     ("decode", dict(num_ranks=2, tokens_per_rank=8192, hidden=8)),
     # one-launch dispatch: slots placed in groups of 4, 2 and 1 (k = 7)
     ("wide", dict(num_ranks=16, tokens_per_rank=8, hidden=64, experts_per_rank=4, top_k=7)),
-    # one-launch dispatch at its limits (256 assignments per rank, 1024 in all), and just past
-    ("decode", dict(num_ranks=4, tokens_per_rank=256, hidden=256)),
-    ("decode", dict(num_ranks=4, tokens_per_rank=257, hidden=256)),
+    # one-launch dispatch at its limits (256 assignments per rank, 2048 in all), and just
+    # past each of them
+    ("decode", dict(num_ranks=8, tokens_per_rank=256, hidden=256)),
+    ("decode", dict(num_ranks=8, tokens_per_rank=257, hidden=256)),
+    ("decode", dict(num_ranks=16, tokens_per_rank=129, hidden=256)),
     # a small receive capacity (rows dropped, flagged, counts kept)
     ("wide", dict(num_ranks=4, tokens_per_rank=30, hidden=64, experts_per_rank=2, top_k=2,
                   recv_capacity_rows=20)),
@@ -140,10 +142,10 @@ def test_repeated_ids_within_a_token_are_sent_k_times(path):
     _full_oracle_check(w, x, ids, gates, path)
 
 
-# Steps of at most 1024 assignments (and at most 256 per rank) dispatch in one launch that
+# Steps of at most 2048 assignments (and at most 256 per rank) dispatch in one launch that
 # places rows by counting over the ids; larger ones plan first.  Cases that probe error
 # handling run on both sides of that line.
-SIDES = [24, 200]
+SIDES = [24, 300]
 SIDE_IDS = ["one-launch", "planned"]
 
 
