@@ -62,16 +62,18 @@ def test_host_side_rejections_enqueue_nothing():
             a2av.a2av_create(bad)
 
 
-# 64 tokens per rank: one-launch dispatch (512 assignments); 300: planned (2400)
-@pytest.mark.parametrize("tokens", [64, 300], ids=["one-launch", "planned"])
+# 64 tokens per rank: one-launch dispatch (512 assignments), with 4 KB rows also with
+# each row's count split over a block's wavefronts; 300: planned (2400)
+@pytest.mark.parametrize("tokens,hidden", [(64, 96), (64, 2048), (300, 96)],
+                         ids=["one-launch", "one-launch-split-count", "planned"])
 @pytest.mark.parametrize("layout", [a2av.LAYOUT_SOURCE_MAJOR, a2av.LAYOUT_EXPERT_MAJOR], ids=["srcmaj", "expmaj"])
 @pytest.mark.parametrize("path", [a2av.PATH_STAGED, a2av.PATH_DIRECT], ids=["staged", "direct"])
-def test_receive_overflow_keeps_guard_rows_and_true_counts(path, layout, tokens):
-    w = W.workload("wide", num_ranks=4, tokens_per_rank=tokens, hidden=96, experts_per_rank=2, top_k=2)
+def test_receive_overflow_keeps_guard_rows_and_true_counts(path, layout, tokens, hidden):
+    w = W.workload("wide", num_ranks=4, tokens_per_rank=tokens, hidden=hidden, experts_per_rank=2, top_k=2)
     x, ids, gates = W.make_inputs(w)
     full = oracle.dispatch(oracle.as_rows(x), ids, w.experts_per_rank, w.capacity)
     cap = int(full["recv_off"][:, w.num_ranks].max()) - 7
-    w = W.workload("wide", num_ranks=4, tokens_per_rank=tokens, hidden=96, experts_per_rank=2, top_k=2,
+    w = W.workload("wide", num_ranks=4, tokens_per_rank=tokens, hidden=hidden, experts_per_rank=2, top_k=2,
                    recv_capacity_rows=cap)
     banner(f"overflow: cap {cap} rows per rank")
     xt, idt, gt = to_device(w, x, ids, gates)

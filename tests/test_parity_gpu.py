@@ -84,8 +84,10 @@ SMALL = [
     ("edge", dict(num_ranks=1024, tokens_per_rank=2, hidden=16, routing="uniform")),
     # long runs per wavefront: 8192 assignments per rank spread over 16 wavefronts
     ("decode", dict(num_ranks=2, tokens_per_rank=8192, hidden=8)),
-    # one-launch dispatch: slots placed in groups of 4, 2 and 1 (k = 7)
+    # one-launch dispatch: slots placed in groups of 4, 2 and 1 (k = 7); with 4 KB rows
+    # cut into 4 pieces, each row's count split over the block's four wavefronts
     ("wide", dict(num_ranks=16, tokens_per_rank=8, hidden=64, experts_per_rank=4, top_k=7)),
+    ("wide", dict(num_ranks=4, tokens_per_rank=16, hidden=2048, experts_per_rank=4, top_k=7)),
     # one-launch dispatch at its limits (256 assignments per rank, 2048 in all), and just
     # past each of them
     ("decode", dict(num_ranks=8, tokens_per_rank=256, hidden=256)),
@@ -145,14 +147,13 @@ def test_repeated_ids_within_a_token_are_sent_k_times(path):
 # Steps of at most 2048 assignments (and at most 256 per rank) dispatch in one launch that
 # places rows by counting over the ids; larger ones plan first.  Cases that probe error
 # handling run on both sides of that line.
-SIDES = [24, 300]
-SIDE_IDS = ["one-launch", "planned"]
 
 
-@pytest.mark.parametrize("tokens", SIDES, ids=SIDE_IDS)
+@pytest.mark.parametrize("tokens,hidden", [(24, 128), (16, 2048), (300, 128)],
+                         ids=["one-launch", "one-launch-split-count", "planned"])
 @pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
-def test_out_of_range_ids_are_dropped_and_flagged(path, tokens):
-    w = W.workload("wide", num_ranks=4, tokens_per_rank=tokens, hidden=128, experts_per_rank=4, top_k=2)
+def test_out_of_range_ids_are_dropped_and_flagged(path, tokens, hidden):
+    w = W.workload("wide", num_ranks=4, tokens_per_rank=tokens, hidden=hidden, experts_per_rank=4, top_k=2)
     x, ids, gates = W.make_inputs(w)
     ids = ids.copy()
     ids[0, 3, 1] = w.num_experts
