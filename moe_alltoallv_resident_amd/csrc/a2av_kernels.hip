@@ -17,11 +17,11 @@
 //             reading the return buffer (staged) or the expert outputs in place (direct).
 // Everything but planning is a row copy or gather bound by HBM bandwidth: rows move as
 // 16-byte vectors, one 64-lane wavefront per row, with all of a row's loads issued
-// before its stores, non-temporal for buffers too large to stay in cache.  Nothing here
-// is a dense contraction, so no matrix-core instruction is used.  Small steps (decode
-// sizes) are bound by launches and dependent table reads instead of bytes; there plan,
-// tables and pack run as one launch in which every block works from the routing ids
-// (dispatch_small_kernel).
+// before its stores, stores non-temporal, loads non-temporal for buffers too large to
+// stay in cache.  Nothing here is a dense contraction, so no matrix-core instruction is
+// used.  Small steps (decode sizes) are bound by launches and dependent table reads
+// instead of bytes; there plan, tables and pack run as one launch in which every block
+// works from the routing ids (dispatch_small_kernel).
 #include "a2av_internal.h"
 
 #include <algorithm>
@@ -394,7 +394,7 @@ __device__ __forceinline__ void copy_row(V* __restrict__ dst, const V* __restric
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int v = base + u * kWave + lane;
-            if (v < v1) st<NT>(dst + v, r[u]);
+            if (v < v1) st<true>(dst + v, r[u]);
         }
     }
 }
@@ -485,7 +485,7 @@ __global__ void __launch_bounds__(kBlock) pack_kernel(const V* __restrict__ x, V
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int v = base + u * kWave + lane;
-                if (v < pc.v1) st<NT>(row + v, r[u]);
+                if (v < pc.v1) st<true>(row + v, r[u]);
             }
         }
     }
@@ -726,7 +726,7 @@ __global__ void __launch_bounds__(kBlock) dispatch_small_kernel(const V* __restr
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int v = base + u * kWave + lane;
-                if (v < pc.v1) st<false>(row + v, r[u]);
+                if (v < pc.v1) st<true>(row + v, r[u]);
             }
         }
         base += kWave * U;
@@ -921,7 +921,7 @@ __global__ void __launch_bounds__(kBlock) combine_kernel(const typename Vec<B>::
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int v = base + u * kWave + lane;
-            if (v < pc.v1) st<NT>(out + v, El::pack(acc[u]));
+            if (v < pc.v1) st<true>(out + v, El::pack(acc[u]));
         }
     }
 }
@@ -995,9 +995,12 @@ __global__ void __launch_bounds__(1024) route_step_kernel(const int32_t* __restr
 // ---- launch helpers ------------------------------------------------------------------
 inline unsigned row_blocks(int64_t rows) { return (unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock); }
 
-// Non-temporal row traffic once a kernel's rows are far larger than the caches (the
-// 256 MiB last-level cache); small decode-sized steps keep rows cacheable so that the
-// next kernel can hit them.
+// Row loads are non-temporal once a kernel's rows are far larger than the caches (the
+// 256 MiB last-level cache); smaller steps keep them cacheable.  Row stores are always
+// non-temporal: no kernel reads back what it writes, and a kernel ends only after its
+// XCDs' L2s have written back every dirty line, which at decode sizes costs more than
+// the stores themselves (measured: non-temporal stores take about 1 us off each decode
+// launch that writes 10 MB).
 constexpr int64_t kStreamBytes = 256ll << 20;
 
 template <typename F>
