@@ -31,9 +31,12 @@ def _tables(w, steps):
 
 @pytest.mark.parametrize("path,layout", [(a2av.PATH_STAGED, 0), (a2av.PATH_DIRECT, 0), (a2av.PATH_DIRECT, 1)],
                          ids=["staged", "direct", "direct-expmaj"])
-@pytest.mark.parametrize("name,steps,full_every", [("decode", 100, 10), ("edge", 24, 1)])
-def test_graph_replay_with_device_side_routing(name, steps, full_every, path, layout):
-    w = W.workload(name)
+# decode and edge dispatch in one launch; the 512-token decode plans first
+@pytest.mark.parametrize("name,over,steps,full_every", [("decode", {}, 100, 10), ("edge", {}, 24, 1),
+                                                        ("decode", dict(tokens_per_rank=512), 24, 8)],
+                         ids=["decode", "edge", "decode-planned"])
+def test_graph_replay_with_device_side_routing(name, over, steps, full_every, path, layout):
+    w = W.workload(name, **over)
     banner(f"graph replay {w.describe()} steps={steps} path={path} layout={layout}")
     x = W.make_x(w)
     ids_tab, gates_tab = _tables(w, steps)
