@@ -16,7 +16,9 @@ per-kernel event times, `stage_us` their breakdown); `ms_per_step` is a whole st
 (expert stand-in included).  `roofline` is for the slowest kernel of the step, from its
 per-kernel event time; `cpu_baseline` is the CPU oracle on a bounded sample of
 the same workload; `decode_graph` and `edge_graph` are the decode and edge shapes
-captured in hipGraphs and replayed with routing that changes on the device each step.
+captured in hipGraphs and replayed with routing that changes on the device each step;
+`graph_kernel_node_us` is what one nearly empty dependent kernel adds to a replayed
+graph step (the launch gap).
 """
 import argparse
 import json
@@ -196,6 +198,7 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.no_decode_graph:
+        result["graph_kernel_node_us"] = graph_kernel_node_us(torch, a2av)
         result["decode_graph"] = {p: decode_graph(np, torch, a2av, W, p) for p in paths}
         result["edge_graph"] = {p: decode_graph(np, torch, a2av, W, p, workload="edge") for p in paths}
 
@@ -419,6 +422,48 @@ def decode_graph(np, torch, a2av, W, path, workload="decode", steps=100, per_gra
     s.close()
     torch.cuda.empty_cache()
     return out
+
+
+def graph_kernel_node_us(torch, a2av, nodes=8, per_graph=10, replays=20):
+    """What one kernel node costs inside a replayed graph when it has nearly nothing to
+    do: graphs of `per_graph` steps, each step a chain of 1 or `nodes` launches of the
+    router stand-in with no ids to copy; the difference per step over nodes - 1 is the
+    launch gap a dependent kernel adds at decode sizes."""
+    t = torch.zeros(1, dtype=torch.int32, device="cuda")
+    g = torch.zeros(1, dtype=torch.float32, device="cuda")
+    counter = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def per_step_us(m):
+        def step():
+            for _ in range(m):
+                a2av.a2av_route_step(t, g, 1, 0, counter, t, g)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(per_graph):
+                step()
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        trials = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(replays):
+                graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            trials.append(e0.elapsed_time(e1) * 1e3 / (replays * per_graph))
+        del graph
+        return sorted(trials)[2]
+
+    one, many = per_step_us(1), per_step_us(nodes)
+    return round((many - one) / (nodes - 1), 3)
 
 
 def cpu_baseline(np, W, w, sample_tokens):
