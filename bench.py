@@ -18,7 +18,8 @@ per-kernel event time; `cpu_baseline` is the CPU oracle on a bounded sample of
 the same workload; `decode_graph` and `edge_graph` are the decode and edge shapes
 captured in hipGraphs and replayed with routing that changes on the device each step;
 `graph_kernel_node_us` is what one nearly empty dependent kernel adds to a replayed
-graph step (the launch gap).
+graph step (the launch gap); `wide` is the top-8 shape (16 x 2048 tokens, hidden 7168,
+256 experts) timed the same way as the headline, 10 steps per path.
 """
 import argparse
 import json
@@ -94,6 +95,8 @@ def main():
     ap.add_argument("--workload", default="prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode-graph", action="store_true")
+    ap.add_argument("--no-wide", action="store_true",
+                    help="skip the top-8 wide shape (16 x 2048 tokens, hidden 7168) timed after the headline")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--paths", default="staged,direct,direct-expert-major",
                     help="paths to time (staged, direct, staged-expert-major, direct-expert-major); "
@@ -196,6 +199,21 @@ def main():
                                                  if k not in ("ms_per_step_wall", "ms_per_step_full")}
     del xt
     torch.cuda.empty_cache()
+
+    if not args.no_wide and w.name != "wide":
+        ww = W.workload("wide")
+        log(f"workload {ww.describe()}; generating inputs")
+        xw, idw, gw = W.make_inputs(ww)
+        xwt = torch.from_numpy(xw.view(np.int16)).view(torch.bfloat16).cuda()
+        idwt, gwt = torch.from_numpy(idw).cuda(), torch.from_numpy(gw).cuda()
+        wide = {}
+        for p in paths:
+            m = time_path(torch, a2av, ww, xwt, idwt, gwt, p, 10, 3)
+            wide[p] = {k: m[k] for k in ("us_per_step", "us_per_step_min", "GBps", "pct_hbm_peak", "bytes_per_step",
+                                         "stage_us")}
+        result["wide"] = {"workload": ww.describe(), "steps": 10, "warmup": 3, "paths": wide}
+        del xwt, idwt, gwt
+        torch.cuda.empty_cache()
 
     if not args.no_decode_graph:
         result["graph_kernel_node_us"] = graph_kernel_node_us(torch, a2av)
