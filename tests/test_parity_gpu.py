@@ -149,6 +149,21 @@ def test_repeated_ids_within_a_token_are_sent_k_times(path):
 # handling run on both sides of that line.
 
 
+@pytest.mark.parametrize("tokens", [128, 600], ids=["one-launch", "planned"])
+@pytest.mark.parametrize("layout", LAYOUTS, ids=LAYOUT_IDS)
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
+def test_every_token_routed_to_the_same_two_experts(path, layout, tokens):
+    # the most skewed step: one rank receives everything, every other split is empty,
+    # and all assignments hit the same two (expert, sender) counters
+    w = W.workload("tiny", num_ranks=4, tokens_per_rank=tokens, hidden=512, dtype=W.BF16, experts_per_rank=2,
+                   top_k=2, expert_mode=W.EXPERT_SCALE)
+    x, _, gates = W.make_inputs(w)
+    ids = np.empty((4, tokens, 2), dtype=np.int32)
+    ids[..., 0], ids[..., 1] = 5, 4
+    ref = _full_oracle_check(w, x, ids, gates, path, layout)
+    assert int(ref["recv_off"][2, 4]) == 4 * tokens * 2
+
+
 @pytest.mark.parametrize("tokens,hidden", [(24, 128), (16, 2048), (300, 128)],
                          ids=["one-launch", "one-launch-split-count", "planned"])
 @pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
