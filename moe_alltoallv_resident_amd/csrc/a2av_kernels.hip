@@ -31,6 +31,8 @@ namespace {
 
 constexpr int kWave = 64;
 constexpr int kRowsPerBlock = 4;     // 256-thread blocks, one wavefront per row
+constexpr int kBigRowsPerBlock = 16; // 1024-thread blocks for the streaming (non-temporal) row
+                                     // copies (pack, exchange): measured 1-4 % faster than 256
 constexpr int kBlock = kWave * kRowsPerBlock;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -431,20 +433,20 @@ __device__ __forceinline__ int segment_of(const int32_t* so, int R, int64_t p, i
 
 // pack: row x[s][t] to its k places: the sender's send buffer (staged) or the
 // receivers' buffers (direct).  The blocks after the row blocks build the receive tables.
-template <typename V, int U, bool NT, bool DIRECT>
-__global__ void __launch_bounds__(kBlock) pack_kernel(const V* __restrict__ x, V* __restrict__ dst, Shape sh,
-                                                      Tables tb, Outputs out, uint32_t* status, Split sp) {
+template <typename V, int U, bool NT, bool DIRECT, int RPB>
+__global__ void __launch_bounds__(RPB * kWave) pack_kernel(const V* __restrict__ x, V* __restrict__ dst, Shape sh,
+                                                           Tables tb, Outputs out, uint32_t* status, Split sp) {
     const int lane = lane_id();
-    const int64_t rblk = ((int64_t)sh.R * sh.T * sp.cpr + kRowsPerBlock - 1) / kRowsPerBlock;
+    const int64_t rblk = ((int64_t)sh.R * sh.T * sp.cpr + RPB - 1) / RPB;
     if ((int64_t)blockIdx.x >= rblk) {
-        const int64_t d = ((int64_t)blockIdx.x - rblk) * kRowsPerBlock + threadIdx.x / kWave;
+        const int64_t d = ((int64_t)blockIdx.x - rblk) * RPB + threadIdx.x / kWave;
         if (d < sh.R) {
             write_recv_tables(sh, tb, out, status, (int)d, lane);
             if (sh.layout) write_expert_major_tables(sh, tb, (int)d, lane);
         }
         return;
     }
-    const Piece pc = piece_of((int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kWave, sp);
+    const Piece pc = piece_of((int64_t)blockIdx.x * RPB + threadIdx.x / kWave, sp);
     const int64_t n = pc.row;
     if (n >= (int64_t)sh.R * sh.T) return;
     const int64_t s = n / sh.T;
@@ -744,9 +746,10 @@ __global__ void __launch_bounds__(kBlock) dispatch_small_kernel(const V* __restr
 // back to the send places and writes zeros where a row was dropped.  FIRST: this is the
 // first kernel after planning (the bare collective), so the first blocks build the
 // receive tables and rows find their receive offset from the send offsets.
-template <typename V, int U, bool NT, bool REVERSE, bool FIRST>
-__global__ void __launch_bounds__(kBlock) exchange_kernel(const V* __restrict__ src, V* __restrict__ dst, Shape sh,
-                                                          Tables tb, Outputs out, uint32_t* status, Split sp) {
+template <typename V, int U, bool NT, bool REVERSE, bool FIRST, int RPB>
+__global__ void __launch_bounds__(RPB * kWave) exchange_kernel(const V* __restrict__ src, V* __restrict__ dst,
+                                                               Shape sh, Tables tb, Outputs out, uint32_t* status,
+                                                               Split sp) {
     const int lane = lane_id();
     int64_t blk = blockIdx.x;
     if constexpr (FIRST) {
@@ -758,7 +761,7 @@ __global__ void __launch_bounds__(kBlock) exchange_kernel(const V* __restrict__ 
         }
         blk -= tblk;
     }
-    const Piece pc = piece_of(blk * kRowsPerBlock + threadIdx.x / kWave, sp);
+    const Piece pc = piece_of(blk * RPB + threadIdx.x / kWave, sp);
     const int64_t g = pc.row;
     if (g >= (int64_t)sh.R * sh.TK) return;
     const int R = sh.R;
@@ -840,8 +843,8 @@ template <int B, int DT> struct Elems {
 // combine: y[s][t] = round(sum_j g_j * row_j) with one float32 FMA per slot in slot
 // order, starting from 0.  row_j is the returned row at send place pos_j (staged) or
 // the expert output in the receiver's buffer (direct).
-template <int B, int DT, int U, bool NT, bool DIRECT, bool PAIRS>
-__global__ void __launch_bounds__(kBlock) combine_kernel(const typename Vec<B>::T* __restrict__ rows,
+template <int B, int DT, int U, bool NT, bool DIRECT, bool PAIRS, int RPB>
+__global__ void __launch_bounds__(RPB * kWave) combine_kernel(const typename Vec<B>::T* __restrict__ rows,
                                                          const float* __restrict__ gates,
                                                          typename Vec<B>::T* __restrict__ y, Shape sh, Tables tb,
                                                          Split sp) {
@@ -849,7 +852,7 @@ __global__ void __launch_bounds__(kBlock) combine_kernel(const typename Vec<B>::
     using El = Elems<B, DT>;
     constexpr int NE = El::N;
     const int lane = lane_id();
-    const Piece pc = piece_of((int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kWave, sp);
+    const Piece pc = piece_of((int64_t)blockIdx.x * RPB + threadIdx.x / kWave, sp);
     const int64_t n = pc.row;
     if (n >= (int64_t)sh.R * sh.T) return;
     const int64_t s = n / sh.T;
@@ -970,10 +973,10 @@ __global__ void __launch_bounds__(kBlock) expert_kernel(const typename Vec<B>::T
 
 // Reference row copy (measurement harness): the same row movement as the exchange with
 // the identity mapping, for the achievable-bandwidth line next to the path's kernels.
-template <int U, bool NT>
-__global__ void __launch_bounds__(kBlock) reference_copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
-                                                                int64_t rows, Split sp) {
-    const Piece pc = piece_of((int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kWave, sp);
+template <int U, bool NT, int RPB>
+__global__ void __launch_bounds__(RPB * kWave) reference_copy_kernel(const u32x4* __restrict__ src,
+                                                                     u32x4* __restrict__ dst, int64_t rows, Split sp) {
+    const Piece pc = piece_of((int64_t)blockIdx.x * RPB + threadIdx.x / kWave, sp);
     if (pc.row >= rows) return;
     copy_row<u32x4, U, NT>(dst + pc.row * sp.nvec, src + pc.row * sp.nvec, pc.v0, pc.v1, lane_id());
 }
@@ -1093,7 +1096,6 @@ hipError_t launch_pack(const Shape& sh, const Tables& tb, const Outputs& out, ui
                        void* dst, bool direct, int vec, hipStream_t st) {
     const int64_t N = (int64_t)sh.R * sh.T;
     const Split sp = make_split(sh.row_bytes, vec, N, sh.num_cu);
-    const unsigned grid = (unsigned)(table_blocks(sh.R) + piece_blocks(N, sp));
     const int64_t bytes = N * sh.row_bytes;
     return with_vec(vec, [&](auto B) {
         using V = typename Vec<decltype(B)::value>::T;
@@ -1101,12 +1103,14 @@ hipError_t launch_pack(const Shape& sh, const Tables& tb, const Outputs& out, ui
             return with_nt(bytes, [&](auto NT) {
                 constexpr int u = decltype(U)::value;
                 constexpr bool nt = decltype(NT)::value;
+                constexpr int rpb = nt ? kBigRowsPerBlock : kRowsPerBlock;
+                const unsigned grid = (unsigned)((N * sp.cpr + rpb - 1) / rpb + (sh.R + rpb - 1) / rpb);
                 if (direct)
-                    hipLaunchKernelGGL((pack_kernel<V, u, nt, true>), dim3(grid), dim3(kBlock), 0, st, (const V*)x,
-                                       (V*)dst, sh, tb, out, status, sp);
+                    hipLaunchKernelGGL((pack_kernel<V, u, nt, true, rpb>), dim3(grid), dim3(rpb * kWave), 0, st,
+                                       (const V*)x, (V*)dst, sh, tb, out, status, sp);
                 else
-                    hipLaunchKernelGGL((pack_kernel<V, u, nt, false>), dim3(grid), dim3(kBlock), 0, st, (const V*)x,
-                                       (V*)dst, sh, tb, out, status, sp);
+                    hipLaunchKernelGGL((pack_kernel<V, u, nt, false, rpb>), dim3(grid), dim3(rpb * kWave), 0, st,
+                                       (const V*)x, (V*)dst, sh, tb, out, status, sp);
                 return hipGetLastError();
             });
         });
@@ -1158,15 +1162,23 @@ hipError_t launch_exchange(const Shape& sh, const Tables& tb, const Outputs& out
             return with_nt(bytes, [&](auto NT) {
                 constexpr int u = decltype(U)::value;
                 constexpr bool nt = decltype(NT)::value;
+                constexpr int big = kBigRowsPerBlock;
+                const unsigned gbig = (unsigned)((rows * sp.cpr + big - 1) / big);
                 if (first)
-                    hipLaunchKernelGGL((exchange_kernel<V, u, nt, false, true>), dim3(grid), dim3(kBlock), 0, st,
-                                       (const V*)src, (V*)dst, sh, tb, out, status, sp);
+                    hipLaunchKernelGGL((exchange_kernel<V, u, nt, false, true, kRowsPerBlock>), dim3(grid),
+                                       dim3(kBlock), 0, st, (const V*)src, (V*)dst, sh, tb, out, status, sp);
+                else if (reverse && nt)
+                    hipLaunchKernelGGL((exchange_kernel<V, u, nt, true, false, big>), dim3(gbig), dim3(big * kWave), 0,
+                                       st, (const V*)src, (V*)dst, sh, tb, out, status, sp);
                 else if (reverse)
-                    hipLaunchKernelGGL((exchange_kernel<V, u, nt, true, false>), dim3(grid), dim3(kBlock), 0, st,
-                                       (const V*)src, (V*)dst, sh, tb, out, status, sp);
+                    hipLaunchKernelGGL((exchange_kernel<V, u, nt, true, false, kRowsPerBlock>), dim3(grid),
+                                       dim3(kBlock), 0, st, (const V*)src, (V*)dst, sh, tb, out, status, sp);
+                else if (nt)
+                    hipLaunchKernelGGL((exchange_kernel<V, u, nt, false, false, big>), dim3(gbig), dim3(big * kWave),
+                                       0, st, (const V*)src, (V*)dst, sh, tb, out, status, sp);
                 else
-                    hipLaunchKernelGGL((exchange_kernel<V, u, nt, false, false>), dim3(grid), dim3(kBlock), 0, st,
-                                       (const V*)src, (V*)dst, sh, tb, out, status, sp);
+                    hipLaunchKernelGGL((exchange_kernel<V, u, nt, false, false, kRowsPerBlock>), dim3(grid),
+                                       dim3(kBlock), 0, st, (const V*)src, (V*)dst, sh, tb, out, status, sp);
                 return hipGetLastError();
             });
         });
@@ -1187,20 +1199,22 @@ static hipError_t launch_combine_t(const Shape& sh, const Tables& tb, const void
             constexpr int NE = Elems<B, DT>::N, U0 = decltype(U)::value;
             constexpr int U1 = U0 * NE > 64 ? 64 / NE : U0, UK = U0 * NE > 32 ? 32 / NE : U0;
             constexpr bool nt = decltype(NT)::value;
-            const unsigned grid = piece_blocks(N, sp);
+            constexpr int rpb = kRowsPerBlock;   // measured: 1024-thread blocks make the combine ~6 % slower
+            const unsigned grid = (unsigned)((N * sp.cpr + rpb - 1) / rpb);
+            const dim3 block(rpb * kWave);
             if (sh.k == 1) {
                 if (direct)
-                    hipLaunchKernelGGL((combine_kernel<B, DT, U1, nt, true, false>), dim3(grid), dim3(kBlock), 0, st,
+                    hipLaunchKernelGGL((combine_kernel<B, DT, U1, nt, true, false, rpb>), dim3(grid), block, 0, st,
                                        (const V*)rows, gates, (V*)y, sh, tb, sp);
                 else
-                    hipLaunchKernelGGL((combine_kernel<B, DT, U1, nt, false, false>), dim3(grid), dim3(kBlock), 0, st,
+                    hipLaunchKernelGGL((combine_kernel<B, DT, U1, nt, false, false, rpb>), dim3(grid), block, 0, st,
                                        (const V*)rows, gates, (V*)y, sh, tb, sp);
             } else {
                 if (direct)
-                    hipLaunchKernelGGL((combine_kernel<B, DT, UK, nt, true, true>), dim3(grid), dim3(kBlock), 0, st,
+                    hipLaunchKernelGGL((combine_kernel<B, DT, UK, nt, true, true, rpb>), dim3(grid), block, 0, st,
                                        (const V*)rows, gates, (V*)y, sh, tb, sp);
                 else
-                    hipLaunchKernelGGL((combine_kernel<B, DT, UK, nt, false, true>), dim3(grid), dim3(kBlock), 0, st,
+                    hipLaunchKernelGGL((combine_kernel<B, DT, UK, nt, false, true, rpb>), dim3(grid), block, 0, st,
                                        (const V*)rows, gates, (V*)y, sh, tb, sp);
             }
             return hipGetLastError();
@@ -1263,9 +1277,11 @@ hipError_t launch_reference_copy(const void* src, void* dst, int64_t rows, int64
     const Split sp = make_split(row_bytes, 16, rows, num_cu);
     return with_unroll(sp.cv, [&](auto U) {
         return with_nt(rows * row_bytes, [&](auto NT) {
-            hipLaunchKernelGGL((reference_copy_kernel<decltype(U)::value, decltype(NT)::value>),
-                               dim3(piece_blocks(rows, sp)), dim3(kBlock), 0, st, (const u32x4*)src, (u32x4*)dst, rows,
-                               sp);
+            constexpr bool nt = decltype(NT)::value;
+            constexpr int rpb = nt ? kBigRowsPerBlock : kRowsPerBlock;
+            hipLaunchKernelGGL((reference_copy_kernel<decltype(U)::value, nt, rpb>),
+                               dim3((unsigned)((rows * sp.cpr + rpb - 1) / rpb)), dim3(rpb * kWave), 0, st,
+                               (const u32x4*)src, (u32x4*)dst, rows, sp);
             return hipGetLastError();
         });
     });
