@@ -34,7 +34,7 @@
  *     enqueued).
  *   - Problems only the GPU can see (an expert id outside [0, E), a rank receiving
  *     more rows than its capacity) OR bits into the caller's device word `*status`
- *     (sticky; the library never clears or reads it).  No write ever goes out of
+ *     (sticky; the library never clears or reads it; it must be 4-byte aligned).  No write ever goes out of
  *     bounds: a dropped assignment is not sent, a row past the capacity is not
  *     written, and either adds zero to the combine.  Counts stay true.
  *   - A handle serves one dispatch/combine pair at a time: combine uses the routing

@@ -219,9 +219,12 @@ int a2av_destroy(a2av_handle_t h) {
     return rc;
 }
 
+// The status word is updated with device atomics, which need a 4-byte aligned address.
+static bool status_ok(const uint32_t* status) { return status && ((uintptr_t)status % 4) == 0; }
+
 int a2av_dispatch(a2av_handle_t h, const void* x, const int32_t* topk_ids, void* recv, int32_t* split,
                   int32_t* recv_counts, int32_t* recv_offsets, uint32_t* status, void* stream) {
-    if (!h || !status || !on_device(h)) return A2AV_ERR_INVALID;
+    if (!h || !status_ok(status) || !on_device(h)) return A2AV_ERR_INVALID;
     const Shape& sh = h->sh;
     if (has_tokens(sh) && (!x || !topk_ids || (sh.cap > 0 && !recv))) return A2AV_ERR_INVALID;
     const void* ptrs[] = {x, recv, h->send_buf};
@@ -256,7 +259,7 @@ int a2av_dispatch(a2av_handle_t h, const void* x, const int32_t* topk_ids, void*
 
 int a2av_combine(a2av_handle_t h, const void* expert_out, const float* gates, void* y, uint32_t* status,
                  void* stream) {
-    if (!h || !status || !on_device(h) || !h->routed) return A2AV_ERR_INVALID;
+    if (!h || !status_ok(status) || !on_device(h) || !h->routed) return A2AV_ERR_INVALID;
     const Shape& sh = h->sh;
     if (has_tokens(sh) && (!gates || !y || (sh.cap > 0 && !expert_out))) return A2AV_ERR_INVALID;
     const void* ptrs[] = {expert_out, y, h->send_buf};
@@ -279,7 +282,7 @@ int a2av_combine(a2av_handle_t h, const void* expert_out, const float* gates, vo
 
 int a2av_alltoallv(a2av_handle_t h, const void* send, const int32_t* send_counts, void* recv, int32_t* recv_counts,
                    int32_t* recv_offsets, uint32_t* status, void* stream) {
-    if (!h || !send_counts || !status || !on_device(h)) return A2AV_ERR_INVALID;
+    if (!h || !send_counts || !status_ok(status) || !on_device(h)) return A2AV_ERR_INVALID;
     const Shape& sh = h->sh;
     if (has_tokens(sh) && (!send || (sh.cap > 0 && !recv))) return A2AV_ERR_INVALID;
     const void* ptrs[] = {send, recv};

@@ -44,6 +44,10 @@ def test_host_side_rejections_enqueue_nothing():
     # misaligned row data (float32 rows need 4-byte alignment)
     assert L.a2av_dispatch(h, vp(xt.data_ptr() + 2), P(idt), P(recv), None, None, None, P(st),
                            stream) == a2av.ERR_INVALID
+    # a status word the device atomics cannot update (not 4-byte aligned)
+    st8 = torch.zeros(2, dtype=torch.int32, device="cuda")
+    assert L.a2av_dispatch(h, P(xt), P(idt), P(recv), None, None, None, vp(st8.data_ptr() + 2),
+                           stream) == a2av.ERR_INVALID
     # bad expert stand-in mode
     a2av.a2av_dispatch(h, xt, idt, recv, None, None, None, st)
     assert L.a2av_expert_apply(h, P(recv), P(recv), 7, stream) == a2av.ERR_INVALID
