@@ -503,9 +503,10 @@ __global__ void __launch_bounds__(RPB * kWave) pack_kernel(const V* __restrict__
 //   next table_blocks(R)   receiver tables, counted from the ids;
 //   from `lead` on         rows: each wavefront finds where its token's k assignments
 //                          go by counting the assignments that come before them in the
-//                          destination's order, and copies the row there.
+//                          destination's order (the block's four wavefronts split the
+//                          count when they hold pieces of one row), and copies the row.
 // `lead` is a multiple of 8, so a row keeps the block number (and with it the XCD) it
-// has in the combine.
+// has in the combine.  Row stores are non-temporal, as everywhere.
 
 // The step's ids, copied into LDS by the whole block (one round of loads).
 __device__ __forceinline__ void stage_ids(const int32_t* __restrict__ ids, int64_t A, int* sids) {
