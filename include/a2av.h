@@ -81,7 +81,7 @@ typedef struct a2av_context* a2av_handle_t;
 /* return codes */
 #define A2AV_OK           0
 #define A2AV_ERR_INVALID (-1)   /* argument or configuration rejected */
-#define A2AV_ERR_NOMEM   (-2)   /* device allocation failed (create only) */
+#define A2AV_ERR_NOMEM   (-2)   /* allocation failed (create; timing_begin on the host) */
 #define A2AV_ERR_HIP     (-3)   /* a HIP runtime call or launch failed */
 
 /* device status bits, OR-ed into *status */
@@ -217,16 +217,19 @@ int a2av_route_step(const int32_t* ids_table, const float* gates_table, int32_t 
 int a2av_copy_reference(const void* src, void* dst, int64_t rows, int64_t row_bytes, void* stream);
 
 /* Stage timing with HIP events recorded between the library's kernels on the call's
- * stream.  a2av_timing_begin(h, max_calls) creates events for up to max_calls
+ * stream.  a2av_timing_begin(h, max_calls), 1 <= max_calls <= A2AV_TIMING_MAX_CALLS,
+ * creates events for up to max_calls
  * dispatch and max_calls combine calls (host-side event objects only; no device
  * memory); later calls record until the budget is used.  a2av_timing_end waits for
  * the recorded events, writes per-stage sums of milliseconds into ms_sum (host)
  * [A2AV_STAGES] and the number of timed launches per stage into launches (host)
  * [A2AV_STAGES], and releases the events.  Stages: 0 plan (histogram + scans), 1 pack,
- * 2 exchange, 3 return exchange, 4 combine (the direct path has no 2 and 3; the
- * expert-major layout adds a second, small launch to stage 0).  Events
- * recorded between kernels add a little time to each step while timing is on. */
+ * 2 exchange, 3 return exchange, 4 combine (the direct path has no 2 and 3; a
+ * dispatch that runs as one launch counts it as stage 1 and has no stage 0).  Events
+ * recorded between kernels add a little time to each step while timing is on.
+ * a2av_timing_begin returns A2AV_ERR_NOMEM if the host cannot hold the events. */
 #define A2AV_STAGES 5
+#define A2AV_TIMING_MAX_CALLS (1 << 20)
 int a2av_timing_begin(a2av_handle_t h, int32_t max_calls);
 int a2av_timing_end(a2av_handle_t h, double* ms_sum, int32_t* launches);
 

@@ -149,7 +149,7 @@ const char* a2av_error_string(int code) {
     switch (code) {
         case A2AV_OK: return "ok";
         case A2AV_ERR_INVALID: return "invalid argument or configuration";
-        case A2AV_ERR_NOMEM: return "device allocation failed";
+        case A2AV_ERR_NOMEM: return "allocation failed";
         case A2AV_ERR_HIP: return "HIP runtime error";
         default: return "unknown error code";
     }
@@ -352,9 +352,13 @@ int a2av_copy_reference(const void* src, void* dst, int64_t rows, int64_t row_by
 }
 
 int a2av_timing_begin(a2av_handle_t h, int32_t max_calls) {
-    if (!h || max_calls < 1) return A2AV_ERR_INVALID;
+    if (!h || max_calls < 1 || max_calls > A2AV_TIMING_MAX_CALLS) return A2AV_ERR_INVALID;
     drop_timing(h);
-    h->timed.resize((size_t)max_calls * A2AV_STAGES);
+    try {
+        h->timed.resize((size_t)max_calls * A2AV_STAGES);
+    } catch (const std::bad_alloc&) {
+        return A2AV_ERR_NOMEM;
+    }
     for (TimedLaunch& t : h->timed) {
         t.a = t.b = nullptr;
         if (hipEventCreate(&t.a) != hipSuccess || hipEventCreate(&t.b) != hipSuccess) {

@@ -48,6 +48,9 @@ def test_host_side_rejections_enqueue_nothing():
     st8 = torch.zeros(2, dtype=torch.int32, device="cuda")
     assert L.a2av_dispatch(h, P(xt), P(idt), P(recv), None, None, None, vp(st8.data_ptr() + 2),
                            stream) == a2av.ERR_INVALID
+    # stage timing budgets outside 1 .. A2AV_TIMING_MAX_CALLS
+    assert L.a2av_timing_begin(h, 0) == a2av.ERR_INVALID
+    assert L.a2av_timing_begin(h, (1 << 20) + 1) == a2av.ERR_INVALID
     # bad expert stand-in mode
     a2av.a2av_dispatch(h, xt, idt, recv, None, None, None, st)
     assert L.a2av_expert_apply(h, P(recv), P(recv), 7, stream) == a2av.ERR_INVALID
