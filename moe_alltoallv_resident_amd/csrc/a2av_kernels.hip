@@ -500,7 +500,7 @@ __global__ void __launch_bounds__(RPB * kWave) pack_kernel(const V* __restrict__
 // no block reads what another block of the launch writes; every block works from the
 // routing ids directly:
 //   blocks [0, R)          planning of one rank each (the tables later kernels use);
-//   next table_blocks(R)   receiver tables, counted from the ids;
+//   next R                 one receiver's tables each, counted from the ids;
 //   from `lead` on         rows: each wavefront finds where its token's k assignments
 //                          go by counting the assignments that come before them in the
 //                          destination's order (the block's four wavefronts split the
@@ -563,17 +563,19 @@ __device__ __forceinline__ void count_places(const Shape& sh, const int* sids, i
     }
 }
 
-// Receiver d's tables counted from the ids (in LDS) by one wavefront into `hist`
+// Receiver d's tables counted from the ids (in LDS) by the whole block into `hist`
 // (epr x R ints of LDS, zeroed by the caller): hist[le * R + s] = rows sender s sends to
 // d's local expert le, by LDS atomic increments (independent of one another, so they
 // pipeline; a loop that waits on LDS every step is slow here, where the row
-// wavefronts keep the LDS busy).  count_tables_write then forms recv_counts / recv_off
-// as write_recv_tables does and, for expert-major buffers, xbase and recv_eoff as
+// wavefronts keep the LDS busy).  Each thread takes every blockDim.x-th id (measured at
+// 64 receivers x 2048 ids: one wavefront per receiver left the table blocks ~0.8 us
+// behind the rows).  count_tables_write then forms recv_counts / recv_off as
+// write_recv_tables does and, for expert-major buffers, xbase and recv_eoff as
 // write_expert_major_tables does; the caller puts a block barrier between the two.
-__device__ __forceinline__ void count_tables_fill(const Shape& sh, const int* sids, int d, int lane, int* hist) {
+__device__ __forceinline__ void count_tables_fill(const Shape& sh, const int* sids, int d, int* hist) {
     const int A = sh.R * (int)sh.TK, TK = (int)sh.TK;
     const int elo = d * sh.epr;
-    for (int i = lane; i < A; i += kWave) {
+    for (int i = threadIdx.x; i < A; i += blockDim.x) {
         const int le = sids[i] - elo;
         if (le >= 0 && le < sh.epr) atomicAdd(&hist[le * sh.R + i / TK], 1);
     }
@@ -623,10 +625,10 @@ __device__ void count_tables_write(const Shape& sh, const Tables& tb, const Outp
 }
 
 // LDS (ints) of the one-launch dispatch: planning needs 5 rows of E counters, a table
-// block 4 histograms of E plus the ids, a row block the ids and its wavefronts' partial
+// block one histogram of E plus the ids, a row block the ids and its wavefronts' partial
 // counts (4 x 64).
 __host__ __device__ __forceinline__ int64_t small_lds_ints(int64_t E, int64_t A) {
-    const int64_t plan = (kRowsPerBlock + 1) * E, tables = kRowsPerBlock * E + A;
+    const int64_t plan = (kRowsPerBlock + 1) * E, tables = E + A;
     const int64_t rows = A + kRowsPerBlock * kMaxTopK;
     const int64_t m = plan > tables ? plan : tables;
     return m > rows ? m : rows;
@@ -645,16 +647,17 @@ __global__ void __launch_bounds__(kBlock) dispatch_small_kernel(const V* __restr
         plan_rank<1>(a, blockIdx.x, lds, wsum);
         return;
     }
-    if ((int)blockIdx.x < lead) {                   // receiver tables
-        const int64_t d = ((int64_t)blockIdx.x - R) * kRowsPerBlock + w;
-        int* hist = lds + w * sh.E;                 // epr x R = E ints per wavefront
-        int* sids = lds + kRowsPerBlock * sh.E;
-        for (int i = lane; i < sh.E; i += kWave) hist[i] = 0;
+    if ((int)blockIdx.x < lead) {                   // receiver d's tables
+        const int d = (int)blockIdx.x - R;
+        if (d >= R) return;                         // padding up to `lead` (whole block)
+        int* hist = lds;                            // epr x R = E ints
+        int* sids = lds + sh.E;
+        for (int i = threadIdx.x; i < sh.E; i += blockDim.x) hist[i] = 0;
         stage_ids(a.ids, A, sids);
         __syncthreads();
-        if (d < R) count_tables_fill(sh, sids, (int)d, lane, hist);
+        count_tables_fill(sh, sids, d, hist);
         __syncthreads();
-        if (d < R) count_tables_write(sh, a.tb, a.out, a.status, (int)d, lane, hist);
+        if (w == 0) count_tables_write(sh, a.tb, a.out, a.status, d, lane, hist);
         return;
     }
     const Piece pc = piece_of(((int64_t)blockIdx.x - lead) * kRowsPerBlock + w, sp);
@@ -1135,7 +1138,7 @@ hipError_t launch_dispatch_small(const Shape& sh, const Tables& tb, const int32_
                                  uint32_t* status, const void* x, void* dst, bool direct, int vec, hipStream_t st) {
     const int64_t N = (int64_t)sh.R * sh.T;
     const Split sp = make_split(sh.row_bytes, vec, N, sh.num_cu);
-    const int lead = (int)((sh.R + table_blocks(sh.R) + 7) / 8 * 8);
+    const int lead = (2 * sh.R + 7) / 8 * 8;   // planning and table blocks, padded to a multiple of 8
     const unsigned grid = (unsigned)(lead + piece_blocks(N, sp));
     const size_t lds = (size_t)small_lds_ints(sh.E, (int64_t)sh.R * sh.TK) * sizeof(int);
     const PlanArgs a{sh, tb, out, ids, status};
