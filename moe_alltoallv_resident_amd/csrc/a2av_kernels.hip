@@ -535,11 +535,20 @@ __device__ __forceinline__ void count_places(const Shape& sh, const int* sids, i
     const int slice = (hi - lo + parts - 1) / parts;
     lo += part * slice;
     hi = min(hi, lo + slice);
-    int elo[NS], ehi[NS];
+    // Branch-free test (short-circuit conditions compile to an exec-mask branch per id run
+    // and slot, which made the count the slowest part of the launch): id i counts for
+    // slot j when it is scanned, names one of the slot's candidate experts (one unsigned
+    // range compare), and either belongs to a whole earlier sender or precedes the slot
+    // in (expert, index) order.  That order is one unsigned key, expert << 16 | index -
+    // before: the offset is below 2^16 (at most 2048 assignments) and only ids inside the
+    // expert range, all below 2^15, have their key compared.
+    unsigned elo[NS], span[NS], kme[NS];
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
-        elo[j] = e[j] >= 0 ? (DIRECT ? d[j] * sh.epr : 0) : 1;
-        ehi[j] = e[j] >= 0 ? (DIRECT ? elo[j] + sh.epr : sh.E) : 0;   // empty range: counts nothing
+        const bool some = e[j] >= 0;
+        elo[j] = some && DIRECT ? (unsigned)(d[j] * sh.epr) : 0u;
+        span[j] = some ? (unsigned)(DIRECT ? sh.epr : sh.E) : 0u;   // 0: counts nothing
+        kme[j] = ((unsigned)e[j] << 16) | (unsigned)(me0 + j - before);
         q[j] = 0;
     }
     constexpr int kRuns = 4;   // 64-id runs read before any is used
@@ -553,10 +562,11 @@ __device__ __forceinline__ void count_places(const Shape& sh, const int* sids, i
 #pragma unroll
         for (int u = 0; u < kRuns; ++u) {
             const int i = i0 + u * kWave + lane;
+            const bool live = i < hi, early = i < before;
+            const unsigned key = ((unsigned)v[u] << 16) | (unsigned)(i - before);
 #pragma unroll
             for (int j = 0; j < NS; ++j) {
-                const bool hit = i < hi && v[u] >= elo[j] && v[u] < ehi[j] &&
-                                 (i < before || v[u] < e[j] || (v[u] == e[j] && i < me0 + j));
+                const bool hit = live & ((unsigned)v[u] - elo[j] < span[j]) & (early | (key < kme[j]));
                 q[j] += __popcll(__ballot(hit));
             }
         }
