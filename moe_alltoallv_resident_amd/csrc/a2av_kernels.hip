@@ -586,8 +586,8 @@ __device__ __forceinline__ void count_tables_fill(const Shape& sh, const int* si
     const int A = sh.R * (int)sh.TK, TK = (int)sh.TK;
     const int elo = d * sh.epr;
     for (int i = threadIdx.x; i < A; i += blockDim.x) {
-        const int le = sids[i] - elo;
-        if (le >= 0 && le < sh.epr) atomicAdd(&hist[le * sh.R + i / TK], 1);
+        const unsigned le = (unsigned)sids[i] - (unsigned)elo;   // any int32 id: no signed overflow
+        if (le < (unsigned)sh.epr) atomicAdd(&hist[(int)le * sh.R + i / TK], 1);
     }
 }
 

@@ -174,6 +174,12 @@ def test_out_of_range_ids_are_dropped_and_flagged(path, tokens, hidden):
     ids[0, 3, 1] = w.num_experts
     ids[2, 0, 0] = -1
     ids[3, tokens - 1, 1] = 1 << 30
+    # ids whose low 16 bits (or the value shifted left by 16) equal a valid expert's, and
+    # the int32 extremes: they must be dropped like any other, never taken for that expert
+    ids[1, 2, 0] = (1 << 16) + 3
+    ids[1, 5, 1] = -(1 << 16)
+    ids[0, 7, 0] = np.iinfo(np.int32).min
+    ids[2, 4, 1] = np.iinfo(np.int32).max
     ref = _full_oracle_check(w, x, ids, gates, path)
     assert ref["status"] == oracle.ST_EXPERT_RANGE
 
