@@ -120,11 +120,15 @@ __device__ __forceinline__ int seg_len(const int32_t* send_off, int R, int s, in
 
 // recv_off[d][s] computed from the senders' send offsets (whole wavefront, uniform
 // result): the rows d receives from the senders before s.
+// Index searches read their table entries unconditionally, at an index clamped into the
+// table, and mask the result: a read guarded by a lane condition compiles to a branch
+// with a wait of its own.
 __device__ __forceinline__ int64_t recv_base(const int32_t* send_off, int R, int d, int s, int lane) {
     int acc = 0;
     for (int c0 = 0; c0 < s; c0 += kWave) {
         const int sp = c0 + lane;
-        if (sp < s) acc += seg_len(send_off, R, sp, d);
+        const int c = seg_len(send_off, R, min(sp, s - 1), d);
+        acc += sp < s ? c : 0;
     }
     return wave_sum(acc);
 }
@@ -318,7 +322,8 @@ __device__ __forceinline__ int expert_of(const Shape& sh, const Tables& tb, int6
     int le = 0;
     for (int c0 = 0; c0 < sh.epr; c0 += kWave) {
         const int i = c0 + lane;
-        le += __popcll(__ballot(i < sh.epr && (int64_t)eo[i + 1] <= p));
+        const int64_t end = eo[min(i, sh.epr - 1) + 1];
+        le += __popcll(__ballot((i < sh.epr) & (end <= p)));
     }
     return d * sh.epr + le;
 }
@@ -338,12 +343,14 @@ __device__ __forceinline__ int64_t expert_major_place_counted(const Shape& sh, c
                                                               int64_t p, int d, int lane) {
     const int e = expert_of(sh, tb, s, p, d, lane);
     const int R = sh.R, E = sh.E, epr = sh.epr, le = e - d * epr;
-    const int pairs = epr * R;
+    // pair i = l2 * R + s2 comes before (le, s) exactly when i < le * R + s
+    const int lim = le * R + (int)s;
     int acc = 0;
-    for (int c0 = 0; c0 < pairs; c0 += kWave) {
-        const int i = c0 + lane;
+    for (int c0 = 0; c0 < lim; c0 += kWave) {
+        const int i = min(c0 + lane, lim - 1);
         const int l2 = i / R, s2 = i - l2 * R;
-        if (i < pairs && (l2 < le || (l2 == le && s2 < s))) acc += tb.cnt[(int64_t)s2 * E + d * epr + l2];
+        const int c = tb.cnt[(int64_t)s2 * E + d * epr + l2];
+        acc += c0 + lane < lim ? c : 0;
     }
     return (int64_t)wave_sum(acc) + (p - tb.eoff[s * (E + 1) + e]);
 }
@@ -426,7 +433,8 @@ __device__ __forceinline__ int segment_of(const int32_t* so, int R, int64_t p, i
     int d = 0;
     for (int c0 = 0; c0 < R; c0 += kWave) {
         const int i = c0 + lane;
-        d += __popcll(__ballot(i < R && (int64_t)so[i + 1] <= p));
+        const int64_t end = so[min(i, R - 1) + 1];
+        d += __popcll(__ballot((i < R) & (end <= p)));
     }
     return d;
 }
