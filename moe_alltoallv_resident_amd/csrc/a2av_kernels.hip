@@ -951,10 +951,47 @@ __global__ void __launch_bounds__(RPB * kWave) combine_kernel(const typename Vec
     }
 }
 
+// The g-th written receive row of an expert-major buffer, taking receivers in order
+// and each receiver's rows front to back (so expert group after expert group): receiver
+// d holds n_d = min(rows received, capacity) written rows, the row is q = g - (n_0 + ...
+// + n_{d-1}) of the first d whose prefix passes g, and its expert is the local expert
+// whose group [recv_eoff[d][le], recv_eoff[d][le + 1]) holds q.  False past the last
+// written row.  (Whole wavefront; the result is uniform.)
+__device__ bool grouped_row(const Shape& sh, const Tables& tb, int64_t g, int lane, int64_t* row, int* e) {
+    const int R = sh.R, epr = sh.epr;
+    int64_t carry = 0;
+    for (int c0 = 0; c0 < R; c0 += kWave) {
+        const int d = c0 + lane;
+        const int64_t got = tb.recv_off[(int64_t)min(d, R - 1) * (R + 1) + R];
+        const int n = d < R ? (int)(got < sh.cap ? got : sh.cap) : 0;
+        const int incl = wave_inclusive_scan(n);
+        const uint64_t past = __builtin_amdgcn_ballot_w64(carry + incl > g);
+        if (past) {
+            const int dl = __builtin_ctzll(past);
+            const int dd = c0 + dl;
+            const int64_t q = g - carry - __shfl(incl - n, dl, kWave);
+            const int32_t* eo = tb.recv_eoff + (int64_t)dd * (epr + 1);
+            int le = 0;
+            for (int l0 = 0; l0 < epr; l0 += kWave) {
+                const int l = l0 + lane;
+                const int64_t end = eo[min(l, epr - 1) + 1];
+                le += __popcll(__builtin_amdgcn_ballot_w64((l < epr) & (end <= q)));
+            }
+            *row = (int64_t)dd * sh.cap + q;
+            *e = dd * epr + le;
+            return true;
+        }
+        carry += __shfl(incl, kWave - 1, kWave);
+    }
+    return false;
+}
+
 // Harness expert stand-in over every received row: identity, or scale by 1 + e/256
 // with one rounding (the float32 product of a bf16 value and 1 + e/256 is exact).
-// Rows are found from the send side as in the exchange; the row's expert is the one
-// whose slice of the sender's expert-sorted segment holds it.
+// Expert-major buffers are walked as a grouped expert op walks them: receiver by
+// receiver, each local expert's contiguous group in turn, the expert taken from the
+// group starts.  Source-major rows are found from the send side as in the exchange; the
+// row's expert is the one whose slice of the sender's expert-sorted segment holds it.
 template <int B, int DT, int U>
 __global__ void __launch_bounds__(kBlock) expert_kernel(const typename Vec<B>::T* __restrict__ in,
                                                         typename Vec<B>::T* out, Shape sh, Tables tb, Split sp,
@@ -968,15 +1005,20 @@ __global__ void __launch_bounds__(kBlock) expert_kernel(const typename Vec<B>::T
     if (g >= (int64_t)sh.R * sh.TK) return;
     const int R = sh.R;
     const int nvec = sp.nvec;
-    const int64_t s = g / sh.TK, p = g - s * sh.TK;
-    const int32_t* so = tb.send_off + s * (R + 1);
-    if (p >= so[R]) return;
-    const int d = segment_of(so, R, p, lane);
-    const int e = expert_of(sh, tb, s, p, d, lane);
-    const int64_t q = sh.layout ? (int64_t)tb.xbase[s * sh.E + e] + (p - tb.eoff[s * (sh.E + 1) + e])
-                                : (int64_t)tb.recv_off[(int64_t)d * (R + 1) + s] + (p - so[d]);
-    if (q < 0 || q >= sh.cap) return;
-    const int64_t row = (int64_t)d * sh.cap + q;
+    int64_t row;
+    int e;
+    if (sh.layout) {
+        if (!grouped_row(sh, tb, g, lane, &row, &e)) return;
+    } else {
+        const int64_t s = g / sh.TK, p = g - s * sh.TK;
+        const int32_t* so = tb.send_off + s * (R + 1);
+        if (p >= so[R]) return;
+        const int d = segment_of(so, R, p, lane);
+        e = expert_of(sh, tb, s, p, d, lane);
+        const int64_t q = (int64_t)tb.recv_off[(int64_t)d * (R + 1) + s] + (p - so[d]);
+        if (q < 0 || q >= sh.cap) return;
+        row = (int64_t)d * sh.cap + q;
+    }
     if (mode == 0) {
         if (in != out) copy_row<V, U, false>(out + row * nvec, in + row * nvec, pc.v0, pc.v1, lane);
         return;
