@@ -265,3 +265,47 @@ def _dest_ids(counts, T):
     for s in range(R):
         ids[s, :, 0] = np.repeat(np.arange(R), counts[s])
     return ids
+
+
+@pytest.mark.parametrize("name,over,path,expected", [
+    # planned form: plan, pack, exchange / return, combine (staged); plan, pack / combine (direct)
+    ("decode", dict(tokens_per_rank=300), a2av.PATH_STAGED, [1, 1, 1, 1, 1]),
+    ("decode", dict(tokens_per_rank=300), a2av.PATH_DIRECT, [1, 1, 0, 0, 1]),
+    # one-launch form: its single launch counts as pack
+    ("decode", {}, a2av.PATH_STAGED, [0, 1, 1, 1, 1]),
+    ("decode", {}, a2av.PATH_DIRECT, [0, 1, 0, 0, 1]),
+], ids=["planned-staged", "planned-direct", "one-launch-staged", "one-launch-direct"])
+def test_stage_timing_counts_each_launch_once(name, over, path, expected):
+    """Stage timing records one event pair per library launch while its budget lasts:
+    per step the launches named in include/a2av.h, times non-negative, nothing recorded
+    once the budget is spent."""
+    w = W.workload(name, **over)
+    x, ids, gates = W.make_inputs(w)
+    xt, idt, gt = to_device(w, x, ids, gates)
+    s = a2av.Session(w.num_ranks, w.tokens_per_rank, w.hidden, w.dtype, w.experts_per_rank, w.top_k, path=path)
+    y = torch.empty_like(xt)
+    steps = 3
+    a2av.a2av_timing_begin(s.handle, steps)
+    for _ in range(steps + 2):          # two steps past the budget
+        s.dispatch(xt, idt)
+        s.combine(s.recv, gt, y)
+    ms, launches = a2av.a2av_timing_end(s.handle)
+    assert int(s.status.item()) == 0
+    per_step = sum(expected)
+    budget = steps * a2av.STAGES
+    # the budget holds steps * 5 launches; a step makes per_step of them
+    want = [0] * a2av.STAGES
+    done = 0
+    for _ in range(steps + 2):
+        for i, c in enumerate(expected):
+            if c and done < budget:
+                want[i] += 1
+                done += 1
+    assert launches == want, (launches, want)
+    assert all(m >= 0.0 for m in ms) and all((m > 0.0) == (n > 0) for m, n in zip(ms, launches))
+    # a second window starts from zero
+    a2av.a2av_timing_begin(s.handle, 1)
+    s.dispatch(xt, idt)
+    ms2, launches2 = a2av.a2av_timing_end(s.handle)
+    assert launches2 == [1 if (c and i < 3) else 0 for i, c in enumerate(expected)]
+    s.close()
