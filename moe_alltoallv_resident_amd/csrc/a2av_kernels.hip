@@ -363,27 +363,36 @@ struct CountsArgs {
     uint32_t* status;
 };
 
-__global__ void __launch_bounds__(256) plan_from_counts_kernel(CountsArgs a) {
+__global__ void __launch_bounds__(kBlock) plan_from_counts_kernel(CountsArgs a) {
     __shared__ int sc[kMaxRanks + 1];
     __shared__ int wsum[5];
-    __shared__ int good;
-    const int R = a.sh.R, tid = threadIdx.x, nt = blockDim.x, s = blockIdx.x;
-    for (int d = tid; d < R; d += nt) sc[d] = a.send_counts[(int64_t)s * R + d];
-    __syncthreads();
-    if (tid == 0) {
-        // counts must be non-negative and fit the sender's rows (summed in 64 bits)
-        int64_t sum = 0;
-        bool ok = true;
-        for (int d = 0; d < R; ++d) { ok = ok && sc[d] >= 0; sum += sc[d]; }
-        good = ok && sum <= a.sh.TK;
-        if (!good) atomicOr(a.status, 1u);
+    __shared__ int64_t part[kBlock / kWave];
+    const int R = a.sh.R, tid = threadIdx.x, s = blockIdx.x, lane = lane_id(), w = tid / kWave;
+    // counts must be non-negative and fit the sender's rows: each thread checks and sums
+    // its share in 64 bits, then the block combines the shares
+    int64_t sum = 0;
+    int neg = 0;
+    for (int d = tid; d < R; d += kBlock) {
+        const int c = a.send_counts[(int64_t)s * R + d];
+        sc[d] = c;
+        neg |= c < 0;
+        sum += c;
+    }
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, kWave);
+    if (lane == 0) part[w] = sum;
+    const bool any_neg = __syncthreads_or(neg) != 0;   // also the barrier for part[] and sc[]
+    int64_t total_rows = 0;
+#pragma unroll
+    for (int i = 0; i < kBlock / kWave; ++i) total_rows += part[i];
+    const bool good = !any_neg && total_rows <= a.sh.TK;
+    if (!good) {
+        if (tid == 0) atomicOr(a.status, 1u);
+        for (int d = tid; d < R; d += kBlock) sc[d] = 0;
     }
     __syncthreads();
-    if (!good)
-        for (int d = tid; d < R; d += nt) sc[d] = 0;
-    __syncthreads();
     const int total = block_exclusive_scan(sc, R, wsum);
-    for (int d = tid; d <= R; d += nt) a.tb.send_off[(int64_t)s * (R + 1) + d] = d < R ? sc[d] : total;
+    for (int d = tid; d <= R; d += kBlock) a.tb.send_off[(int64_t)s * (R + 1) + d] = d < R ? sc[d] : total;
 }
 
 // ------------------------------------------------------------------------------------
@@ -1156,7 +1165,7 @@ hipError_t launch_plan(const Shape& sh, const Tables& tb, const int32_t* ids, co
 hipError_t launch_plan_from_counts(const Shape& sh, const Tables& tb, const int32_t* send_counts, uint32_t* status,
                                    hipStream_t st) {
     CountsArgs a{sh, tb, send_counts, status};
-    hipLaunchKernelGGL(plan_from_counts_kernel, dim3(sh.R), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(plan_from_counts_kernel, dim3(sh.R), dim3(kBlock), 0, st, a);
     return hipGetLastError();
 }
 

@@ -118,10 +118,11 @@ def test_receive_overflow_keeps_guard_rows_and_true_counts(path, layout, tokens,
     a2av.a2av_destroy(h)
 
 
-def test_bare_alltoallv_matches_oracle_exchange():
+@pytest.mark.parametrize("R,T,H", [(6, 40, 64), (1024, 3, 16)], ids=["6-ranks", "1024-ranks"])
+def test_bare_alltoallv_matches_oracle_exchange(R, T, H):
     """a2av_alltoallv on pre-sorted send buffers and device counts equals the oracle's
-    exchange of the same rows (ids chosen so that the sort is the identity)."""
-    R, T, H = 6, 40, 64
+    exchange of the same rows (ids chosen so that the sort is the identity); counts that
+    are negative or exceed a sender's rows are flagged and that sender sends nothing."""
     rng = np.random.default_rng(4)
     dest = np.sort(rng.integers(0, R, size=(R, T)), axis=1).astype(np.int32)   # sorted per sender
     dest[2] = 0                                                                 # one sender, one peer
@@ -152,15 +153,20 @@ def test_bare_alltoallv_matches_oracle_exchange():
     with pytest.raises(a2av.A2AVError):
         a2av.a2av_combine(h, recv, torch.ones((R, T, 1), device="cuda"), y, st)
     # bad counts: a negative count and a sender over its rows are flagged and sent as 0
+    # (sender 5's counts would overflow a 32-bit sum)
     bad = send_counts.copy()
     bad[1, 0] = -1
     bad[3, 2] += T
+    bad[5, 0] = np.iinfo(np.int32).max
+    bad[5, 1] = np.iinfo(np.int32).max
     st.zero_()
     a2av.a2av_alltoallv(h, xt, torch.from_numpy(bad).cuda(), recv, rc, ro, st)
     torch.cuda.synchronize()
     assert int(st.item()) == a2av.ST_EXPERT_RANGE
     rch = host_bits(rc)
-    assert np.all(rch[:, 1] == 0) and np.all(rch[:, 3] == 0)
+    assert np.all(rch[:, 1] == 0) and np.all(rch[:, 3] == 0) and np.all(rch[:, 5] == 0)
+    kept = [s for s in range(R) if s not in (1, 3, 5)]
+    assert np.array_equal(rch[:, kept], ref["recv_counts"][:, kept])
     a2av.a2av_destroy(h)
 
 
