@@ -74,12 +74,15 @@ def step_bytes(w, direct):
 
 
 def stage_bytes(w, direct):
-    """Algorithmic bytes per launch of each stage (real rows only).  Index bytes: pack
-    reads each assignment's place (4 B) and, on the direct path, records its receive row
-    (8 B); the combine reads each gate (4 B) and the place (4 B) or receive row (8 B)."""
+    """Algorithmic bytes per launch of each stage (real rows only).  Index bytes: planning
+    reads the ids and writes every place (and, top-1, the inverse: which token sits at
+    each send place); pack reads each assignment's place or its inverse (4 B) and, on the
+    direct path, records its receive row (8 B); the combine reads each gate (4 B) and the
+    place (4 B) or receive row (8 B)."""
     N, A, row = w.tokens, w.assignments, w.row_bytes
     return {
-        "plan": A * 4 + 4 * (w.num_ranks * w.num_experts + w.num_ranks * (w.num_ranks + 1)) + A * 4,
+        "plan": A * 4 + 4 * (w.num_ranks * w.num_experts + w.num_ranks * (w.num_ranks + 1)) + A * 4
+                + (A * 4 if w.top_k == 1 else 0),
         "pack": (N + A) * row + A * (12 if direct else 4),
         "exchange": 2 * A * row,
         "return": 2 * A * row,

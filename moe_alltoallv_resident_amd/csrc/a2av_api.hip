@@ -77,7 +77,7 @@ bool make_shape(const a2av_config_t* c, Shape* sh) {
 }
 
 struct MetaLayout {
-    size_t pos, cnt, send_off, recv_counts, recv_off, eoff, xbase, recv_eoff, dest, total;
+    size_t pos, cnt, send_off, recv_counts, recv_off, eoff, xbase, recv_eoff, dest, inv, total;
 };
 
 MetaLayout meta_layout(const Shape& sh) {
@@ -92,6 +92,7 @@ MetaLayout meta_layout(const Shape& sh) {
     m.xbase = o;       o += align_up(sizeof(int32_t) * (size_t)sh.R * sh.E);
     m.recv_eoff = o;   o += align_up(sizeof(int32_t) * (size_t)sh.R * (sh.epr + 1));
     m.dest = o;        o += align_up(sizeof(int64_t) * (size_t)sh.R * (size_t)std::max<int64_t>(sh.TK, 1));
+    m.inv = o;         o += align_up(sizeof(int32_t) * (size_t)sh.R * (size_t)std::max<int64_t>(sh.TK, 1));
     m.total = o;
     return m;
 }
@@ -196,6 +197,7 @@ int a2av_create(const a2av_config_t* cfg, a2av_handle_t* out) {
     h->tb.xbase = reinterpret_cast<int32_t*>(b + m.xbase);
     h->tb.recv_eoff = reinterpret_cast<int32_t*>(b + m.recv_eoff);
     h->tb.dest = reinterpret_cast<int64_t*>(b + m.dest);
+    h->tb.inv = reinterpret_cast<int32_t*>(b + m.inv);
     // tables start at zero
     if (hipMemset(h->meta, 0, m.total) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
         (void)hipFree(h->meta);

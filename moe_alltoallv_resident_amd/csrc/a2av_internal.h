@@ -34,6 +34,8 @@ struct Tables {
     int32_t* xbase;        // [R][E]    expert-major: receive place of (sender, expert)'s first row
     int32_t* recv_eoff;    // [R][epr+1] expert-major: where each local expert's rows start
     int64_t* dest;         // [R][TK]   direct path: receive row d * cap + q of each (token, slot), -1 none
+    int32_t* inv;          // [R][TK]   top-1 only: the token at each send place (places past the
+                           //           rows sent are not written)
 };
 
 // Optional copies of the tables for the caller (any may be null).
@@ -59,6 +61,10 @@ hipError_t launch_plan_from_counts(const Shape& sh, const Tables& tb, const int3
 bool small_dispatch(const Shape& sh);
 hipError_t launch_dispatch_small(const Shape& sh, const Tables& tb, const int32_t* ids, const Outputs& out,
                                  uint32_t* status, const void* x, void* dst, bool direct, int vec, hipStream_t st);
+// Whether pack runs in gather form (one wavefront per send place, reading the token the
+// planner put there; top-1 only, where it moves no more bytes than the scatter form).
+// Planning writes `inv` exactly when this holds.
+bool gather_pack(const Shape& sh);
 // pack: staged (dst = send buffer) or direct (dst = receive buffer); also builds the
 // receive tables (and the caller's copies in `out`) and, for expert-major buffers, the
 // expert-major places.

@@ -183,6 +183,7 @@ struct PlanArgs {
     Outputs out;
     const int32_t* ids;
     uint32_t* status;
+    bool inverse;   // also write inv (and dest = -1 for dropped slots) for the gather pack
 };
 
 // Planning of rank s by the whole block; lds holds (waves + 1) * E ints, wsum 17.
@@ -259,17 +260,28 @@ __device__ void plan_rank(const PlanArgs& a, int s, int* lds, int* wsum) {
     for (int i = tid; i < nw * E; i += nt) cw[i] += tot[i % E];
     __syncthreads();
 
-    // pass 2: final positions
+    // pass 2: final positions; for the gather pack also the inverse (which assignment
+    // sits at each send place) and, since no send place leads to a dropped slot, its
+    // empty receive row
+    int32_t* inv = a.tb.inv + (int64_t)s * TK;
+    int64_t* dest = a.tb.dest + (int64_t)s * TK;
+    auto put = [&](int64_t i, int p) {
+        pos[i] = p;
+        if (a.inverse) {
+            if (p >= 0) inv[p] = (int32_t)i;
+            else dest[i] = -1;
+        }
+    };
     if (one_batch) {
 #pragma unroll
         for (int u = 0; u < S; ++u) {
             const int64_t i = a0 + u * kWave + lane;
-            if (i < a1) pos[i] = rk[u] >= 0 ? mine[ev[u]] + rk[u] : -1;
+            if (i < a1) put(i, rk[u] >= 0 ? mine[ev[u]] + rk[u] : -1);
         }
     } else {
         for (int64_t i = a0 + lane; i < a1; i += kWave) {
             const int e = ids[i];
-            pos[i] = (e >= 0 && e < E) ? mine[e] + pos[i] : -1;
+            put(i, (e >= 0 && e < E) ? mine[e] + pos[i] : -1);
         }
     }
 }
@@ -512,6 +524,47 @@ __global__ void __launch_bounds__(RPB * kWave) pack_kernel(const V* __restrict__
             }
         }
     }
+}
+
+// pack, gather form (top-1, where the pack is a permutation of the rows): one wavefront
+// per send place p of sender s, reading the token the planner placed there, so that
+// stores go out in place order and only the loads are scattered over the experts' runs
+// (the access shape of the return exchange).  Places past the rows s sends hold nothing
+// and are skipped; the receive tables are built by the blocks after the rows, as in pack.
+template <typename V, int U, bool NT, bool DIRECT, int RPB>
+__global__ void __launch_bounds__(RPB * kWave) pack_gather_kernel(const V* __restrict__ x, V* __restrict__ dst,
+                                                                  Shape sh, Tables tb, Outputs out, uint32_t* status,
+                                                                  Split sp) {
+    const int lane = lane_id();
+    const int64_t rows = (int64_t)sh.R * sh.TK;
+    const int64_t rblk = (rows * sp.cpr + RPB - 1) / RPB;
+    if ((int64_t)blockIdx.x >= rblk) {
+        const int64_t d = ((int64_t)blockIdx.x - rblk) * RPB + threadIdx.x / kWave;
+        if (d < sh.R) {
+            write_recv_tables(sh, tb, out, status, (int)d, lane);
+            if (sh.layout) write_expert_major_tables(sh, tb, (int)d, lane);
+        }
+        return;
+    }
+    const Piece pc = piece_of((int64_t)blockIdx.x * RPB + threadIdx.x / kWave, sp);
+    const int64_t g = pc.row;
+    if (g >= rows) return;
+    const int R = sh.R;
+    const int nvec = sp.nvec;
+    const int64_t s = g / sh.TK, p = g - s * sh.TK;
+    const int32_t* so = tb.send_off + s * (R + 1);
+    if (p >= so[R]) return;                          // not a sent row
+    const int64_t n = s * sh.T + tb.inv[g];          // its token (k = 1: the assignment is the token)
+    int64_t row = g;
+    if constexpr (DIRECT) {
+        const int d = segment_of(so, R, p, lane);    // < R, since p < so[R]
+        const int64_t q = sh.layout ? expert_major_place_counted(sh, tb, s, p, d, lane)
+                                    : recv_base(tb.send_off, R, d, (int)s, lane) + (p - so[d]);
+        row = q < sh.cap ? (int64_t)d * sh.cap + q : -1;   // past capacity: flagged by the tables
+        if (pc.v0 == 0 && lane == 0) tb.dest[n] = row;
+        if (row < 0) return;
+    }
+    copy_row<V, U, NT>(dst + row * nvec, x + n * nvec, pc.v0, pc.v1, lane);
 }
 
 // ---- one-launch dispatch for small steps -------------------------------------------
@@ -1144,7 +1197,7 @@ hipError_t launch_plan(const Shape& sh, const Tables& tb, const int32_t* ids, co
     // barrier and scan work
     const int nw = (int)std::max<int64_t>(1, std::min<int64_t>(plan_waves(sh.E), (sh.TK + kWave - 1) / kWave));
     const size_t lds = (size_t)(nw + 1) * sh.E * sizeof(int);
-    PlanArgs a{sh, tb, out, ids, status};
+    PlanArgs a{sh, tb, out, ids, status, gather_pack(sh)};
     const int64_t per_wave = (sh.TK + nw - 1) / nw;
     const int64_t slices = (per_wave + kWave - 1) / kWave;
     if (slices <= 1) hipLaunchKernelGGL(plan_kernel<1>, dim3(sh.R), dim3(nw * kWave), lds, st, a);
@@ -1163,8 +1216,36 @@ hipError_t launch_plan_from_counts(const Shape& sh, const Tables& tb, const int3
     return hipGetLastError();
 }
 
+bool gather_pack(const Shape& sh) { return sh.k == 1; }
+
+static hipError_t launch_pack_gather(const Shape& sh, const Tables& tb, const Outputs& out, uint32_t* status,
+                                     const void* x, void* dst, bool direct, int vec, hipStream_t st) {
+    const int64_t rows = (int64_t)sh.R * sh.TK;
+    const Split sp = make_split(sh.row_bytes, vec, rows, sh.num_cu);
+    const int64_t bytes = rows * sh.row_bytes;
+    return with_vec(vec, [&](auto B) {
+        using V = typename Vec<decltype(B)::value>::T;
+        return with_unroll(sp.cv, [&](auto U) {
+            return with_nt(bytes, [&](auto NT) {
+                constexpr int u = decltype(U)::value;
+                constexpr bool nt = decltype(NT)::value;
+                constexpr int rpb = kRowsPerBlock;
+                const unsigned grid = (unsigned)((rows * sp.cpr + rpb - 1) / rpb + (sh.R + rpb - 1) / rpb);
+                if (direct)
+                    hipLaunchKernelGGL((pack_gather_kernel<V, u, nt, true, rpb>), dim3(grid), dim3(rpb * kWave), 0,
+                                       st, (const V*)x, (V*)dst, sh, tb, out, status, sp);
+                else
+                    hipLaunchKernelGGL((pack_gather_kernel<V, u, nt, false, rpb>), dim3(grid), dim3(rpb * kWave), 0,
+                                       st, (const V*)x, (V*)dst, sh, tb, out, status, sp);
+                return hipGetLastError();
+            });
+        });
+    });
+}
+
 hipError_t launch_pack(const Shape& sh, const Tables& tb, const Outputs& out, uint32_t* status, const void* x,
                        void* dst, bool direct, int vec, hipStream_t st) {
+    if (gather_pack(sh)) return launch_pack_gather(sh, tb, out, status, x, dst, direct, vec, st);
     const int64_t N = (int64_t)sh.R * sh.T;
     const Split sp = make_split(sh.row_bytes, vec, N, sh.num_cu);
     const int64_t bytes = N * sh.row_bytes;
@@ -1204,7 +1285,7 @@ hipError_t launch_dispatch_small(const Shape& sh, const Tables& tb, const int32_
     const int lead = (2 * sh.R + 7) / 8 * 8;   // planning and table blocks, padded to a multiple of 8
     const unsigned grid = (unsigned)(lead + piece_blocks(N, sp));
     const size_t lds = (size_t)small_lds_ints(sh.E, (int64_t)sh.R * sh.TK) * sizeof(int);
-    const PlanArgs a{sh, tb, out, ids, status};
+    const PlanArgs a{sh, tb, out, ids, status, false};   // the rows here place themselves
     return with_vec(vec, [&](auto B) {
         using V = typename Vec<decltype(B)::value>::T;
         return with_unroll(sp.cv, [&](auto U) {
