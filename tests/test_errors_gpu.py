@@ -11,7 +11,7 @@ import torch
 import oracle
 from moe_alltoallv_resident_amd import a2av
 from moe_alltoallv_resident_amd import workloads as W
-from tests.gpu_util import assert_combine_close, banner, host_bits, to_device
+from tests.gpu_util import assert_combine_close, banner, host_bits, oracle_tables, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -116,6 +116,72 @@ def test_receive_overflow_keeps_guard_rows_and_true_counts(path, layout, tokens,
     oref = oracle.full_step(x, ids, gates, w.experts_per_rank, w.dtype, w.expert_mode, cap, layout)
     assert_combine_close(host_bits(y), oref["y"], w.dtype, "overflow combine")
     a2av.a2av_destroy(h)
+
+
+# Streaming sizes (over 256 MiB per exchange): the top-1 gather pack, the receive-order
+# forward exchange and the non-temporal copies, with the hottest receiver 7 rows over.
+STREAMING_OVERFLOW = [
+    ("prefill", dict(tokens_per_rank=4096)),                                             # 335 MB
+    ("wide", dict(num_ranks=8, tokens_per_rank=2048, hidden=2048, experts_per_rank=32, top_k=8)),   # 537 MB
+]
+
+
+_STREAMING_Y: dict = {}
+
+
+@pytest.mark.parametrize("path", [a2av.PATH_STAGED, a2av.PATH_DIRECT], ids=["staged", "direct"])
+@pytest.mark.parametrize("layout", [a2av.LAYOUT_SOURCE_MAJOR, a2av.LAYOUT_EXPERT_MAJOR], ids=["srcmaj", "expmaj"])
+@pytest.mark.parametrize("name,over", STREAMING_OVERFLOW, ids=["top1", "top8"])
+def test_receive_overflow_at_streaming_sizes(name, over, path, layout):
+    w0 = W.workload(name, **over)
+    x, ids, gates = W.make_inputs(w0)
+    R = w0.num_ranks
+    cap = int(oracle_tables(w0, ids)["recv_off"][:, R].max()) - 7
+    w = W.workload(name, recv_capacity_rows=cap, **over)
+    assert w.tokens * w.top_k * w.row_bytes >= 256 << 20
+    banner(f"streaming overflow: {w.describe()} cap {cap} rows per rank")
+    ref = oracle_tables(w, ids, layout)
+    assert ref["status"] == oracle.ST_RECV_OVERFLOW
+    xt, idt, gt = to_device(w, x, ids, gates)
+    guard = 3
+    big = torch.full((R * cap + 2 * guard, w.hidden), -7.0, dtype=torch.bfloat16, device="cuda")
+    recv = big[guard:guard + R * cap].view(R, cap, w.hidden)
+    split = torch.empty((R, w.num_experts), dtype=torch.int32, device="cuda")
+    rc = torch.empty((R, R), dtype=torch.int32, device="cuda")
+    ro = torch.empty((R, R + 1), dtype=torch.int32, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    h = a2av.a2av_create(_cfg(w, path, layout))
+    a2av.a2av_dispatch(h, xt, idt, recv, split, rc, ro, st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == a2av.ST_RECV_OVERFLOW
+    assert np.array_equal(host_bits(split), ref["cnt"])
+    assert np.array_equal(host_bits(rc), ref["recv_counts"])
+    assert np.array_equal(host_bits(ro), ref["recv_off"])
+    xf = xt.reshape(w.tokens, w.hidden)
+    pattern = big[0, 0].view(torch.int16)
+    for d in range(R):
+        n = min(int(ref["recv_off"][d, R]), cap)
+        tags = torch.from_numpy(ref["recv_tags"][d, :n].astype(np.int64)).cuda()
+        assert torch.equal(recv[d, :n], xf.index_select(0, tags)), f"receive rows of rank {d}"
+        assert bool((recv[d, n:].view(torch.int16) == pattern).all()), f"rows past the count of rank {d}"
+    assert bool((big[:guard].view(torch.int16) == pattern).all())
+    assert bool((big[-guard:].view(torch.int16) == pattern).all())
+    banner("  receive rows bit-exact, nothing written past the capacity")
+    y = torch.empty_like(xt)
+    a2av.a2av_expert_apply(h, recv, recv, a2av.EXPERT_SCALE)
+    a2av.a2av_combine(h, recv, gt, y, st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == a2av.ST_RECV_OVERFLOW
+    a2av.a2av_destroy(h)
+    yb = host_bits(y)
+    del big, recv, xt, idt, gt, y, xf
+    torch.cuda.empty_cache()
+    key = (name, layout)
+    if key not in _STREAMING_Y:             # the oracle's step does not depend on the path
+        _STREAMING_Y.clear()
+        _STREAMING_Y[key] = oracle.full_step(x, ids, gates, w.experts_per_rank, w.dtype, w.expert_mode, cap,
+                                             layout)["y"]
+    assert_combine_close(yb, _STREAMING_Y[key], w.dtype, "streaming overflow combine")
 
 
 @pytest.mark.parametrize("R,T,H", [(6, 40, 64), (1024, 3, 16)], ids=["6-ranks", "1024-ranks"])

@@ -96,6 +96,9 @@ SMALL = [
     # a small receive capacity (rows dropped, flagged, counts kept)
     ("wide", dict(num_ranks=4, tokens_per_rank=30, hidden=64, experts_per_rank=2, top_k=2,
                   recv_capacity_rows=20)),
+    # the same at top-1: the one-launch dispatch, then the planned gather-form pack
+    ("decode", dict(num_ranks=4, tokens_per_rank=30, hidden=64, recv_capacity_rows=20)),
+    ("decode", dict(num_ranks=4, tokens_per_rank=300, hidden=64, recv_capacity_rows=200)),
     # more assignments per wavefront than its registers hold: planning in several batches
     ("wide", dict(num_ranks=2, tokens_per_rank=9000, hidden=16, experts_per_rank=8, top_k=2)),
     ("wide", dict(num_ranks=8, tokens_per_rank=2000, hidden=16, experts_per_rank=512, top_k=4)),
