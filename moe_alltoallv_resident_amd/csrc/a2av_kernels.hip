@@ -1166,6 +1166,16 @@ inline unsigned row_blocks(int64_t rows) { return (unsigned)((rows + kRowsPerBlo
 // launch that writes 10 MB).
 constexpr int64_t kStreamBytes = 256ll << 20;
 
+// At those sizes the path's copy kernels (pack, exchange, return) run at most two
+// 256-thread blocks per CU: each block asks for 64 KiB of dynamic LDS that no kernel
+// touches, so a CU's 160 KiB holds two.  Their registers alone would allow four; with
+// fewer rows in flight per CU, HBM serves their scattered streams faster (same-box A/B
+// on 10 KiB rows: pack 231 -> 218 us, return 219 -> 211 us; on 14 KiB top-8 rows:
+// exchange 1320 -> 1302 us, return 1357 -> 1318 us; three blocks per CU sat in between).
+// The combine, whose loads go one at a time, keeps full occupancy (capped: top-8
+// 778 -> 1155 us), and so does the identity reference copy (capped: 6.28 -> 6.17 TB/s).
+constexpr unsigned kCopyLds = 64u << 10;
+
 template <typename F>
 hipError_t with_nt(int64_t bytes, F&& f) {
     if (bytes >= kStreamBytes) return f(std::true_type{});
@@ -1269,13 +1279,14 @@ static hipError_t launch_pack_gather(const Shape& sh, const Tables& tb, const Ou
             return with_nt(bytes, [&](auto NT) {
                 constexpr int u = decltype(U)::value;
                 constexpr bool nt = decltype(NT)::value;
+                constexpr unsigned lds = nt ? kCopyLds : 0u;   // streaming: two blocks per CU
                 constexpr int rpb = kRowsPerBlock;
                 const unsigned grid = (unsigned)((rows * sp.cpr + rpb - 1) / rpb + (sh.R + rpb - 1) / rpb);
                 if (direct)
-                    hipLaunchKernelGGL((pack_gather_kernel<V, u, nt, true, rpb>), dim3(grid), dim3(rpb * kWave), 0,
+                    hipLaunchKernelGGL((pack_gather_kernel<V, u, nt, true, rpb>), dim3(grid), dim3(rpb * kWave), lds,
                                        st, (const V*)x, (V*)dst, sh, tb, out, status, sp);
                 else
-                    hipLaunchKernelGGL((pack_gather_kernel<V, u, nt, false, rpb>), dim3(grid), dim3(rpb * kWave), 0,
+                    hipLaunchKernelGGL((pack_gather_kernel<V, u, nt, false, rpb>), dim3(grid), dim3(rpb * kWave), lds,
                                        st, (const V*)x, (V*)dst, sh, tb, out, status, sp);
                 return hipGetLastError();
             });
@@ -1295,13 +1306,14 @@ hipError_t launch_pack(const Shape& sh, const Tables& tb, const Outputs& out, ui
             return with_nt(bytes, [&](auto NT) {
                 constexpr int u = decltype(U)::value;
                 constexpr bool nt = decltype(NT)::value;
+                constexpr unsigned lds = nt ? kCopyLds : 0u;   // streaming: two blocks per CU
                 constexpr int rpb = kRowsPerBlock;
                 const unsigned grid = (unsigned)((N * sp.cpr + rpb - 1) / rpb + (sh.R + rpb - 1) / rpb);
                 if (direct)
-                    hipLaunchKernelGGL((pack_kernel<V, u, nt, true, rpb>), dim3(grid), dim3(rpb * kWave), 0, st,
+                    hipLaunchKernelGGL((pack_kernel<V, u, nt, true, rpb>), dim3(grid), dim3(rpb * kWave), lds, st,
                                        (const V*)x, (V*)dst, sh, tb, out, status, sp);
                 else
-                    hipLaunchKernelGGL((pack_kernel<V, u, nt, false, rpb>), dim3(grid), dim3(rpb * kWave), 0, st,
+                    hipLaunchKernelGGL((pack_kernel<V, u, nt, false, rpb>), dim3(grid), dim3(rpb * kWave), lds, st,
                                        (const V*)x, (V*)dst, sh, tb, out, status, sp);
                 return hipGetLastError();
             });
@@ -1354,19 +1366,20 @@ hipError_t launch_exchange(const Shape& sh, const Tables& tb, const Outputs& out
             return with_nt(bytes, [&](auto NT) {
                 constexpr int u = decltype(U)::value;
                 constexpr bool nt = decltype(NT)::value;
+                constexpr unsigned lds = nt ? kCopyLds : 0u;   // streaming: two blocks per CU
                 if (first)
                     hipLaunchKernelGGL((exchange_kernel<V, u, nt, false, true, kRowsPerBlock>), dim3(grid),
-                                       dim3(kBlock), 0, st, (const V*)src, (V*)dst, sh, tb, out, status, sp);
+                                       dim3(kBlock), lds, st, (const V*)src, (V*)dst, sh, tb, out, status, sp);
                 else if (reverse)
                     hipLaunchKernelGGL((exchange_kernel<V, u, nt, true, false, kRowsPerBlock>), dim3(grid),
-                                       dim3(kBlock), 0, st, (const V*)src, (V*)dst, sh, tb, out, status, sp);
+                                       dim3(kBlock), lds, st, (const V*)src, (V*)dst, sh, tb, out, status, sp);
                 else if (!sh.layout && nt)   // streaming sizes only: at decode sizes the extra
                                              // dependent search made the staged step 8 % slower
                     hipLaunchKernelGGL((exchange_recv_order_kernel<V, u, nt, kRowsPerBlock>), dim3(grid), dim3(kBlock),
-                                       0, st, (const V*)src, (V*)dst, sh, tb, sp);
+                                       lds, st, (const V*)src, (V*)dst, sh, tb, sp);
                 else
                     hipLaunchKernelGGL((exchange_kernel<V, u, nt, false, false, kRowsPerBlock>), dim3(grid),
-                                       dim3(kBlock), 0, st, (const V*)src, (V*)dst, sh, tb, out, status, sp);
+                                       dim3(kBlock), lds, st, (const V*)src, (V*)dst, sh, tb, out, status, sp);
                 return hipGetLastError();
             });
         });
