@@ -1175,6 +1175,10 @@ constexpr int64_t kStreamBytes = 256ll << 20;
 // The combine, whose loads go one at a time, keeps full occupancy (capped: top-8
 // 778 -> 1155 us), and so does the identity reference copy (capped: 6.28 -> 6.17 TB/s).
 constexpr unsigned kCopyLds = 64u << 10;
+// The zero-copy top-1 pack, which finds each row's receive place before moving it, does
+// best at three blocks per CU (same-box A/B, 10 KiB rows: 231-235 us at two, 224 us at
+// three, the step 463 -> 460 us).
+constexpr unsigned kDirectPackLds = 48u << 10;
 
 template <typename F>
 hipError_t with_nt(int64_t bytes, F&& f) {
@@ -1283,8 +1287,8 @@ static hipError_t launch_pack_gather(const Shape& sh, const Tables& tb, const Ou
                 constexpr int rpb = kRowsPerBlock;
                 const unsigned grid = (unsigned)((rows * sp.cpr + rpb - 1) / rpb + (sh.R + rpb - 1) / rpb);
                 if (direct)
-                    hipLaunchKernelGGL((pack_gather_kernel<V, u, nt, true, rpb>), dim3(grid), dim3(rpb * kWave), lds,
-                                       st, (const V*)x, (V*)dst, sh, tb, out, status, sp);
+                    hipLaunchKernelGGL((pack_gather_kernel<V, u, nt, true, rpb>), dim3(grid), dim3(rpb * kWave),
+                                       nt ? kDirectPackLds : 0u, st, (const V*)x, (V*)dst, sh, tb, out, status, sp);
                 else
                     hipLaunchKernelGGL((pack_gather_kernel<V, u, nt, false, rpb>), dim3(grid), dim3(rpb * kWave), lds,
                                        st, (const V*)x, (V*)dst, sh, tb, out, status, sp);
