@@ -12,18 +12,24 @@ dispatch+combine time per step; `us_per_step` is that time: the median over 5 tr
 K back-to-back dispatch+combine pairs / K, with events only around each loop, so launch
 gaps count and no event sits between kernels
 (`us_per_step_min` is the fastest trial, `us_per_step_kernels` the sum of the library's
-per-kernel event times, `stage_us` their breakdown); `ms_per_step` is a whole step
-(expert stand-in included).  `roofline` is for the slowest kernel of the step, from its
-per-kernel event time; `cpu_baseline` is the CPU oracle on a bounded sample of
-the same workload; `decode_graph` and `edge_graph` are the decode and edge shapes
-captured in hipGraphs and replayed with routing that changes on the device each step;
-`graph_kernel_node_us` is what one nearly empty dependent kernel adds to a replayed
-graph step (the launch gap); `wide` is the top-8 shape (16 x 2048 tokens, hidden 7168,
-256 experts) timed the same way as the headline, 10 steps per path.
+per-kernel event times, `stage_us` their breakdown); `ms_per_step` is the same
+dispatch+combine time in milliseconds, and `ms_per_step_with_expert_stand_in` a whole
+step with the harness expert between dispatch and combine.  `roofline` is for the
+slowest kernel of the step, from its per-kernel event time; `cpu_baseline` is the CPU
+oracle on the whole workload in a child process pinned to one core; `decode_graph` and
+`edge_graph` are the decode and edge shapes captured in hipGraphs and replayed with
+routing that changes on the device each step, with dispatch and combine measured
+separately next to a reference copy of the same bytes; `graph_kernel_node_us` is what
+one nearly empty dependent kernel adds to a replayed graph step (the launch gap); `wide`
+is the top-8 shape (16 x 2048 tokens, hidden 7168, 256 experts) timed the same way as
+the headline, 10 steps per path, at a receive capacity of twice the mean rows per rank
+(32,768) and at the worst case (262,144 rows per rank, 60 GB), each path with its own
+roofline entry.
 """
 import argparse
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -58,9 +64,9 @@ def measured_traffic(workload, path, kernel):
         sha = kernel_source_sha256()
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256") != sha or rec.get("workload") != workload:
+    if rec.get("kernel_source_sha256") != sha:
         return None
-    b = rec.get("per_launch_bytes", {}).get(path, {}).get(kernel)
+    b = rec.get("workloads", {}).get(workload, {}).get("per_launch_bytes", {}).get(path, {}).get(kernel)
     return None if b is None else int(b["read"] + b["write"])
 
 
@@ -100,7 +106,13 @@ def main():
     ap.add_argument("--no-decode-graph", action="store_true")
     ap.add_argument("--no-wide", action="store_true",
                     help="skip the top-8 wide shape (16 x 2048 tokens, hidden 7168) timed after the headline")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
+    ap.add_argument("--cpu-baseline-child", metavar="WORKLOAD",
+                    help=argparse.SUPPRESS)   # the pinned CPU oracle run (a child of this script)
+    ap.add_argument("--cpu-core", type=int, default=0, help=argparse.SUPPRESS)
+    ap.add_argument("--traffic-json", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="turn rocprofv3 FETCH_SIZE and WRITE_SIZE databases of a run with --workload W "
+                         "--paths staged,direct into per-launch bytes and merge them into "
+                         "profiles/hbm_traffic.json under W (no GPU)")
     ap.add_argument("--paths", default="staged,direct,direct-expert-major",
                     help="paths to time (staged, direct, staged-expert-major, direct-expert-major); "
                          "the first one gives the headline value")
@@ -111,6 +123,12 @@ def main():
     ap.add_argument("--decode-graph-only", type=int, metavar="REPLAYS", default=0,
                     help="only capture the decode step and replay it REPLAYS times (for API tracing)")
     args = ap.parse_args()
+    if args.cpu_baseline_child:
+        cpu_baseline_child(args.cpu_baseline_child, args.cpu_core)
+        return
+    if args.traffic_json:
+        traffic_json(args.workload, *args.traffic_json)
+        return
     if args.profile_summary:
         profile_summary(args.profile_summary)
         return
@@ -180,7 +198,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": head["ms_per_step_full"],
+        "ms_per_step": round(head["us_per_step"] / 1e3, 4),
+        "ms_per_step_with_expert_stand_in": head["ms_per_step_full"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -209,12 +228,17 @@ def main():
         xw, idw, gw = W.make_inputs(ww)
         xwt = torch.from_numpy(xw.view(np.int16)).view(torch.bfloat16).cuda()
         idwt, gwt = torch.from_numpy(idw).cuda(), torch.from_numpy(gw).cuda()
-        wide = {}
-        for p in paths:
-            m = time_path(torch, a2av, ww, xwt, idwt, gwt, p, 10, 3)
-            wide[p] = {k: m[k] for k in ("us_per_step", "us_per_step_min", "GBps", "pct_hbm_peak", "bytes_per_step",
-                                         "stage_us")}
-        result["wide"] = {"workload": ww.describe(), "steps": 10, "warmup": 3, "paths": wide}
+        worst = ww.num_ranks * ww.tokens_per_rank * min(ww.top_k, ww.experts_per_rank)
+        wide = {"workload": ww.describe(), "steps": 10, "warmup": 3}
+        for label, cap in (("capacity_2x_mean", ww.capacity), ("capacity_worst_case", worst)):
+            runs = {}
+            for p in paths:
+                m = time_path(torch, a2av, ww, xwt, idwt, gwt, p, 10, 3, cap=cap)
+                runs[p] = {k: m[k] for k in ("us_per_step", "us_per_step_min", "GBps", "pct_hbm_peak",
+                                             "bytes_per_step", "stage_us", "roofline")}
+            wide[label] = {"recv_capacity_rows_per_rank": cap,
+                           "recv_bytes": ww.num_ranks * cap * ww.row_bytes, "paths": runs}
+        result["wide"] = wide
         del xwt, idwt, gwt
         torch.cuda.empty_cache()
 
@@ -224,7 +248,7 @@ def main():
         result["edge_graph"] = {p: decode_graph(np, torch, a2av, W, p, workload="edge") for p in paths}
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(np, W, w, args.cpu_sample_tokens)
+        result["cpu_baseline"] = cpu_baseline(w)
 
     print(json.dumps(result), flush=True)
 
@@ -236,18 +260,18 @@ def path_config(a2av, name):
     return path, layout
 
 
-def time_path(torch, a2av, w, xt, idt, gt, name, steps, warmup, trials=5):
+def time_path(torch, a2av, w, xt, idt, gt, name, steps, warmup, trials=5, cap=None):
     """One path: warm-up; `steps` steps with HIP events recorded between the library's
     kernels (on the stream they run on) for the per-kernel breakdown and the roofline;
     then `trials` end-to-end runs with events only around the whole loop: `steps`
     dispatch+combine pairs (the headline: median trial, launch gaps included, no event
     between kernels; the minimum beside it), and `steps` full steps with the expert
-    stand-in between them."""
+    stand-in between them.  `cap` overrides the workload's receive capacity."""
     path_id, layout = path_config(a2av, name)
     direct = path_id == a2av.PATH_DIRECT
     path = name
     s = a2av.Session(w.num_ranks, w.tokens_per_rank, w.hidden, w.dtype, w.experts_per_rank, w.top_k,
-                     w.recv_capacity_rows, path=path_id, recv_layout=layout)
+                     w.recv_capacity_rows if cap is None else cap, path=path_id, recv_layout=layout)
     y = torch.empty_like(xt)
 
     def step():
@@ -371,6 +395,20 @@ def decode_graph(np, torch, a2av, W, path, workload="decode", steps=100, per_gra
         route()
         s.dispatch(xt, ids)
 
+    def route_dispatch_expert():
+        route()
+        s.dispatch(xt, ids)
+        s.expert(s.recv, s.recv, w.expert_mode)
+
+    # a reference row copy of the bytes one dispatch (or one combine) moves: it reads N
+    # rows and writes A (the combine reads A and writes N), so (N + A) / 2 rows each way
+    ref_rows = (w.tokens + w.assignments) // 2
+    ref_src = torch.empty((ref_rows, w.row_bytes // 2), dtype=torch.int16, device="cuda")
+    ref_dst = torch.empty_like(ref_src)
+
+    def reference_copy():
+        a2av.a2av_copy_reference(ref_src, ref_dst, ref_rows, w.row_bytes)
+
     def flushed(fn):
         def g():
             flush_buf.fill_(1)
@@ -393,7 +431,7 @@ def decode_graph(np, torch, a2av, W, path, workload="decode", steps=100, per_gra
         torch.cuda.synchronize()
         return graph
 
-    def us_per_step(fn, count, total):
+    def us_per_step(fn, count, total, routed=True):
         """Median over 5 trials of (time of total/count replays) / total."""
         graph = capture(fn, count)
         trials = []
@@ -405,7 +443,7 @@ def decode_graph(np, torch, a2av, W, path, workload="decode", steps=100, per_gra
                 graph.replay()
             e1.record()
             torch.cuda.synchronize()
-            if int(counter.item()) != total:
+            if routed and int(counter.item()) != total:
                 raise RuntimeError("router stand-in did not run once per step")
             trials.append(e0.elapsed_time(e1) * 1e3 / total)
         del graph
@@ -421,25 +459,42 @@ def decode_graph(np, torch, a2av, W, path, workload="decode", steps=100, per_gra
     t_harness = us_per_step(harness, per_graph, steps)
     t_route = us_per_step(route, per_graph, steps)
     t_route_dispatch = us_per_step(route_dispatch, per_graph, steps)
+    t_route_dispatch_expert = us_per_step(route_dispatch_expert, per_graph, steps)
+    t_copy = us_per_step(reference_copy, per_graph, steps, routed=False)
     t_one = us_per_step(full, 1, steps)
     flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     t_full_f = us_per_step(flushed(full), per_graph, steps)
     t_harness_f = us_per_step(flushed(harness), per_graph, steps)
     ok = int(s.status.item()) == 0
+    t_dispatch = t_route_dispatch - t_route
+    t_combine = t_full - t_route_dispatch_expert
+    direct = path_id == a2av.PATH_DIRECT
+    sb = stage_bytes(w, direct)
     out = {"workload": w.describe(), "steps": steps, "steps_per_graph": per_graph,
            "us_per_step_with_expert_and_router": round(t_full, 2),
            "us_router_and_expert_only": round(t_harness, 2),
            "us_dispatch_combine_estimate": round(t_full - t_harness, 2),
-           "us_dispatch_only_estimate": round(t_route_dispatch - t_route, 2),
+           # dispatch: (router, dispatch) minus (router); combine: (router, dispatch, expert,
+           # combine) minus (router, dispatch, expert), so the combine reads rows the expert
+           # kernel has just written, as after a real expert
+           "us_dispatch": round(t_dispatch, 2),
+           "us_combine": round(t_combine, 2),
+           "us_dispatch_plus_combine": round(t_dispatch + t_combine, 2),
+           "reference_copy": {"rows": ref_rows, "bytes": 2 * ref_rows * w.row_bytes, "us": round(t_copy, 2),
+                              "dispatch_gap_us": round(t_dispatch - t_copy, 2),
+                              "combine_gap_us": round(t_combine - t_copy, 2)},
            "us_per_step_one_step_graphs": round(t_one, 2),
            "flushed_512MiB": {"us_per_step_with_expert_and_router": round(t_full_f, 2),
                               "us_router_and_expert_only": round(t_harness_f, 2),
                               "us_dispatch_combine_estimate": round(t_full_f - t_harness_f, 2)},
-           "host_syncs_between_replays": 0, "status_ok": ok,
-           "algorithmic_bytes_per_step": step_bytes(w, path_id == a2av.PATH_DIRECT)}
-    log(f"graph latency ({path}, {workload}): dispatch+combine {t_full - t_harness:.2f} us warm, "
+           "status_ok": ok,
+           "algorithmic_bytes_per_step": step_bytes(w, direct),
+           "algorithmic_bytes_dispatch": sb["pack"] + (sb["exchange"] if not direct else 0),
+           "algorithmic_bytes_combine": sb["combine"] + (sb["return"] if not direct else 0)}
+    log(f"graph latency ({path}, {workload}): dispatch {t_dispatch:.2f} us, combine {t_combine:.2f} us, "
+        f"reference copy of the same bytes {t_copy:.2f} us; dispatch+combine {t_full - t_harness:.2f} us warm, "
         f"{t_full_f - t_harness_f:.2f} us flushed")
-    del flush_buf
+    del flush_buf, ref_src, ref_dst
     s.close()
     torch.cuda.empty_cache()
     return out
@@ -487,39 +542,130 @@ def graph_kernel_node_us(torch, a2av, nodes=8, per_graph=10, replays=20):
     return round((many - one) / (nodes - 1), 3)
 
 
-def cpu_baseline(np, W, w, sample_tokens):
-    """The CPU oracle as it stands (single-threaded C, fp64) on the same workload with
-    fewer tokens per rank: dispatch + return + combine timed (expert stand-in excluded),
-    reported as effective GB/s over the same staged byte count."""
+def cpu_baseline(w):
+    """The CPU oracle as it stands (single-threaded C, fp64) on the whole workload, run in
+    a child process of this script pinned to one core (the first core this process may
+    use) so that it cannot touch the GPU or a second core.  Reported as effective GB/s
+    over the same staged byte count as the GPU figure."""
+    core = min(os.sched_getaffinity(0))
+    log(f"cpu baseline: oracle on {w.describe()}, child process pinned to core {core}")
+    env = dict(os.environ, OMP_NUM_THREADS="1", HIP_VISIBLE_DEVICES="", CUDA_VISIBLE_DEVICES="")
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-baseline-child", w.name,
+                        "--cpu-core", str(core)], capture_output=True, text=True, env=env, timeout=900)
+    if r.returncode != 0:
+        raise RuntimeError(f"cpu baseline child failed ({r.returncode}): {r.stderr[-2000:]}")
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
+def cpu_baseline_child(name, core, reps=3):
+    """Pinned to `core`: generates the workload, allocates and touches every output of the
+    oracle's dispatch, return and combine, then times only those three C calls (the
+    expert stand-in runs between them, untimed), median of `reps` steps."""
+    os.sched_setaffinity(0, {core})
+    import numpy as np
+
     import oracle
-    ws = W.workload(w.name, tokens_per_rank=min(sample_tokens, w.tokens_per_rank))
-    log(f"cpu baseline: oracle on {ws.describe()}")
-    x, ids, gates = W.make_inputs(ws)
+    from moe_alltoallv_resident_amd import workloads as W
+    w = W.workload(name)
+    x, ids, gates = W.make_inputs(w)
+    R, T, H, k, cap = w.num_ranks, w.tokens_per_rank, w.hidden, w.top_k, w.capacity
     rows = oracle.as_rows(x)
+    d = oracle.alloc_dispatch(R, T, k, w.row_bytes, w.experts_per_rank, cap)
+    ret = np.zeros((R, T * k, w.row_bytes), np.uint8)
+    y = np.zeros_like(x)
+    for a in list(d.values()) + [ret, y]:
+        a.fill(0)                                   # touch every page before timing
     times = []
-    for _ in range(3):
+    for _ in range(reps):
         t0 = time.perf_counter()
-        d = oracle.dispatch(rows, ids, ws.experts_per_rank, ws.capacity)
+        oracle.dispatch(rows, ids, w.experts_per_rank, cap, out=d)
         t1 = time.perf_counter()
-        R, cap, H = ws.num_ranks, ws.capacity, ws.hidden
         recv = d["recv"].view(x.dtype).reshape(R, cap, H)
-        z = oracle.expert(recv, d["cnt"], d["recv_off"], ws.experts_per_rank, ws.dtype, ws.expert_mode)
+        z = oracle.expert(recv, d["cnt"], d["recv_off"], w.experts_per_rank, w.dtype, w.expert_mode)
         t2 = time.perf_counter()
-        ret = oracle.return_exchange(oracle.as_rows(z), d["send_off"], d["recv_off"], ws.tokens_per_rank, ws.top_k)
-        oracle.combine(ret.view(x.dtype).reshape(R, -1, H), d["pos"], gates, ws.dtype)
+        oracle.return_exchange(oracle.as_rows(z), d["send_off"], d["recv_off"], T, k, out=ret)
+        oracle.combine(ret.view(x.dtype).reshape(R, T * k, H), d["pos"], gates, w.dtype, out=y)
         t3 = time.perf_counter()
         times.append((t1 - t0) + (t3 - t2))
+        del z, recv
     t = float(np.median(times))
-    gbps = step_bytes(ws, False) / t / 1e9
+    gbps = step_bytes(w, False) / t / 1e9
     try:
         with open("/proc/cpuinfo") as f:
             model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "unknown")
     except OSError:
         model = "unknown"
-    return {"value": round(gbps, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{ws.describe()} ({ws.tokens_per_rank} of {w.tokens_per_rank} tokens per rank), "
-                      f"median of 3, dispatch+return+combine, {t * 1e3:.0f} ms per step",
-            "host_cpu": model, "host_threads_available": os.cpu_count()}
+    print(json.dumps({
+        "value": round(gbps, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": f"the whole workload, {w.describe()} ({T} tokens per rank), staged path, median of {reps} "
+                  f"steps; timed: the oracle's dispatch, return and combine calls only (outputs allocated and "
+                  f"touched beforehand, expert stand-in untimed)",
+        "us_per_step": round(t * 1e6, 1), "pinned_core": core,
+        "affinity_after_pin": sorted(os.sched_getaffinity(0)),
+        "host_cpu": model, "host_threads_available": os.cpu_count()}), flush=True)
+
+
+def traffic_json(workload, fetch_db, write_db):
+    """Per-launch HBM bytes of the path's kernels from a FETCH_SIZE and a WRITE_SIZE pass
+    of `bench.py --workload W --paths staged,direct`, scaled by what the same counters read
+    for torch's device copy of A rows (the largest __amd_rocclr_copyBuffer launch, whose
+    bytes are known), merged into profiles/hbm_traffic.json under the workload."""
+    import sqlite3
+
+    from moe_alltoallv_resident_amd import workloads as W
+    w = W.workload(workload)
+    copy_bytes = w.assignments * w.row_bytes
+
+    def per_kernel(db, counter):
+        c = sqlite3.connect(db)
+        vals = {}
+        for name, gx, val in c.execute("select kernel_name, grid_size_x, value from counters_collection "
+                                       "where counter_name = ?", (counter,)):
+            vals.setdefault((_short_kernel_name(name), gx), []).append(val)
+        return {key: sum(v) / len(v) for key, v in vals.items()}
+
+    fetch, write = per_kernel(fetch_db, "FETCH_SIZE"), per_kernel(write_db, "WRITE_SIZE")
+    copies = [key for key in fetch if key[0] == "__amd_rocclr_copyBuffer"]
+    big = max(copies, key=lambda key: fetch[key])
+    read_factor = copy_bytes / (fetch[big] * 1024.0)
+    write_factor = copy_bytes / (write[big] * 1024.0)
+    stage_of = {"plan_kernel": None, "pack_kernel": "pack", "pack_gather_kernel": "pack",
+                "exchange_recv_order_kernel": "exchange", "combine_kernel": "combine"}
+    out = {"staged": {}, "direct": {}}
+    for (name, gx), kib in fetch.items():
+        base, targs = name.split("<")[0], [a.strip() for a in name.split("<", 1)[-1].rstrip(">").split(",")]
+        if base == "exchange_kernel":
+            stage, direct = ("return" if targs[3] == "true" else "exchange"), False
+        elif base in ("pack_kernel", "pack_gather_kernel"):
+            stage, direct = "pack", targs[3] == "true"
+        elif base == "combine_kernel":
+            stage, direct = "combine", targs[4] == "true"
+        elif base in stage_of:
+            stage, direct = stage_of[base], False
+        else:
+            continue
+        if stage is None or (name, gx) not in write:
+            continue
+        out["direct" if direct else "staged"][stage] = {
+            "read": int(round(kib * 1024.0 * read_factor)),
+            "write": int(round(write[(name, gx)] * 1024.0 * write_factor)),
+            "kernel": name, "grid_x": gx}
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        rec = {}
+    sha = kernel_source_sha256()
+    if rec.get("kernel_source_sha256") != sha:
+        rec = {"kernel_source_sha256": sha, "workloads": {}}
+    rec.setdefault("workloads", {})[workload] = {
+        "calibration": {"copy_bytes_each_way": copy_bytes, "fetch_kib": fetch[big], "write_kib": write[big],
+                        "read_factor": round(read_factor, 5), "write_factor": round(write_factor, 5)},
+        "per_launch_bytes": out}
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec["workloads"][workload], indent=1))
 
 
 def _short_kernel_name(name):

@@ -217,16 +217,38 @@ class Session:
         self.recv_offsets = torch.empty((R, R + 1), dtype=torch.int32, device=self.device)
         self.status = torch.zeros(1, dtype=torch.int32, device=self.device)
 
+    def _check_tensor(self, name, t, dtype, numel):
+        # host-side checks only (no synchronisation): a wrong element type or a short
+        # buffer would otherwise be read or written past its end by the kernels
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch tensor")
+        if t.dtype != dtype:
+            raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+        if t.numel() != numel:
+            raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+        if t.device != self.device and not (t.is_cuda and self.device.index is None):
+            raise ValueError(f"{name} is on {t.device}, the session on {self.device}")
+
     def dispatch(self, x, topk_ids, stream=None):
+        R, T, H, k = self.R, self.T, self.H, self.k
+        self._check_tensor("x", x, self.torch_dtype, R * T * H)
+        self._check_tensor("topk_ids", topk_ids, torch.int32, R * T * k)
         a2av_dispatch(self.handle, x, topk_ids, self.recv, self.split, self.recv_counts, self.recv_offsets,
                       self.status, stream)
         return self.recv
 
     def expert(self, inp, out, mode, stream=None):
+        n = self.R * self.cap * self.H
+        self._check_tensor("expert input", inp, self.torch_dtype, n)
+        self._check_tensor("expert output", out, self.torch_dtype, n)
         a2av_expert_apply(self.handle, inp, out, mode, stream)
         return out
 
     def combine(self, expert_out, gates, y, stream=None):
+        R, T, H, k = self.R, self.T, self.H, self.k
+        self._check_tensor("expert_out", expert_out, self.torch_dtype, R * self.cap * H)
+        self._check_tensor("gates", gates, torch.float32, R * T * k)
+        self._check_tensor("y", y, self.torch_dtype, R * T * H)
         a2av_combine(self.handle, expert_out, gates, y, self.status, stream)
         return y
 

@@ -83,12 +83,21 @@ WORKLOADS = {
                        zipf_s=1.1, steps=100),
     "prefill": Workload("prefill", 8, 8192, 5120, BF16, 16, 1, "zipf", "sigmoid", EXPERT_SCALE,
                         zipf_s=1.2),
-    "wide": Workload("wide", 16, 2048, 7168, BF16, 16, 8, "uniform", "softmax", EXPERT_SCALE),
+    # receive capacity twice the mean rows per rank (2 * 2048 * 8 = 32,768 rows, 470 MB per
+    # rank) rather than the worst case (262,144 rows, 3.76 GB per rank, 60 GB in all)
+    "wide": Workload("wide", 16, 2048, 7168, BF16, 16, 8, "uniform", "softmax", EXPERT_SCALE,
+                     recv_capacity_rows=32768),
     "edge": Workload("edge", 64, 16, 2048, BF16, 1, 2, "edge", "softmax", EXPERT_SCALE),
 }
 
 
 def workload(name: str, **overrides) -> Workload:
+    """A named workload, optionally with fields replaced.  A named workload's receive
+    capacity belongs to its own shape: when the shape changes (ranks, tokens, experts or
+    top-k) and no capacity is given, the worst case is taken."""
+    shape = {"num_ranks", "tokens_per_rank", "experts_per_rank", "top_k"}
+    if shape & set(overrides) and "recv_capacity_rows" not in overrides:
+        overrides = dict(overrides, recv_capacity_rows=0)
     return replace(WORKLOADS[name], **overrides)
 
 

@@ -25,8 +25,16 @@ SOURCE_MAJOR = 0
 EXPERT_MAJOR = 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liba2av_oracle.so")
+# A2AV_ORACLE_SANITIZED=1 selects the AddressSanitizer/UBSan build of the same source
+# (oracle/build.py), for a process started with the sanitizer runtime preloaded.
+_SANITIZED = os.environ.get("A2AV_ORACLE_SANITIZED") == "1"
+_LIB_PATH = os.path.join(_HERE, "liba2av_oracle_san.so" if _SANITIZED else "liba2av_oracle.so")
 _lib = None
+
+
+def library_path() -> str:
+    """The oracle library this process loads."""
+    return _LIB_PATH
 
 
 def _load():
@@ -34,7 +42,7 @@ def _load():
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
             from . import build as _b
-            _b.build()
+            _b.build(sanitize=_SANITIZED)
         lib = ctypes.CDLL(_LIB_PATH)
         i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
         lib.oracle_dispatch.argtypes = [i32, i32, i32, i32, i64, i64, i32] + [vp] * 11
@@ -72,30 +80,41 @@ def as_rows(x: np.ndarray) -> np.ndarray:
     return x.view(np.uint8).reshape(x.shape[:-1] + (x.shape[-1] * x.itemsize,))
 
 
-def dispatch(x_rows: np.ndarray, ids: np.ndarray, experts_per_rank: int, cap: int, layout: int = SOURCE_MAJOR):
+def alloc_dispatch(R: int, T: int, k: int, row_bytes: int, experts_per_rank: int, cap: int) -> dict:
+    """Zeroed output arrays of ``dispatch`` (to pass as its ``out``)."""
+    E = R * experts_per_rank
+    return dict(
+        cnt=np.zeros((R, E), np.int32),
+        send_off=np.zeros((R, R + 1), np.int32),
+        pos=np.zeros((R, T, k), np.int32),
+        send=np.zeros((R, T * k, row_bytes), np.uint8),
+        recv_counts=np.zeros((R, R), np.int32),
+        recv_off=np.zeros((R, R + 1), np.int32),
+        recv_eoff=np.zeros((R, experts_per_rank + 1), np.int32),
+        recv=np.zeros((R, cap, row_bytes), np.uint8),
+    )
+
+
+def dispatch(x_rows: np.ndarray, ids: np.ndarray, experts_per_rank: int, cap: int, layout: int = SOURCE_MAJOR,
+             out: dict = None):
     """Sort by expert into send buffers, then the all-to-allv.
 
     x_rows: [R][T][row_bytes] uint8 (see ``as_rows``); ids: [R][T][k] int32.
     Returns a dict with cnt [R][E], send_off [R][R+1], pos [R][T][k], send [R][T*k][row],
     recv_counts [R][R] ([dst][src]), recv_off [R][R+1], recv_eoff [R][epr+1],
-    recv [R][cap][row] (source- or expert-major), status.
+    recv [R][cap][row] (source- or expert-major), status.  ``out`` (from
+    ``alloc_dispatch``) supplies the output arrays instead of fresh zeroed ones: only the
+    receive rows a dispatch places are written, so rows past them keep what they held.
     """
     x_rows = _c(x_rows, np.uint8)
     ids = _c(ids, np.int32)
     R, T, k = ids.shape
     assert x_rows.shape[:2] == (R, T)
     row = x_rows.shape[2]
-    E = R * experts_per_rank
-    out = dict(
-        cnt=np.zeros((R, E), np.int32),
-        send_off=np.zeros((R, R + 1), np.int32),
-        pos=np.zeros((R, T, k), np.int32),
-        send=np.zeros((R, T * k, row), np.uint8),
-        recv_counts=np.zeros((R, R), np.int32),
-        recv_off=np.zeros((R, R + 1), np.int32),
-        recv_eoff=np.zeros((R, experts_per_rank + 1), np.int32),
-        recv=np.zeros((R, cap, row), np.uint8),
-    )
+    if out is None:
+        out = alloc_dispatch(R, T, k, row, experts_per_rank, cap)
+    else:
+        assert out["recv"].shape == (R, cap, row) and out["send"].shape == (R, T * k, row)
     st = np.zeros(1, np.uint32)
     rc = _load().oracle_dispatch(R, T, k, experts_per_rank, row, cap, layout, _p(x_rows), _p(ids),
                                  _p(out["cnt"]), _p(out["send_off"]), _p(out["pos"]), _p(out["send"]),
@@ -124,14 +143,20 @@ def expert(recv: np.ndarray, cnt: np.ndarray, recv_off: np.ndarray, experts_per_
 
 
 def return_exchange(z_rows: np.ndarray, send_off: np.ndarray, recv_off: np.ndarray, T: int, k: int,
-                    cnt: np.ndarray = None, experts_per_rank: int = 1, layout: int = SOURCE_MAJOR) -> np.ndarray:
-    """Return all-to-all.  z_rows: [R][cap][row] uint8.  Returns ret [R][T*k][row] uint8.
+                    cnt: np.ndarray = None, experts_per_rank: int = 1, layout: int = SOURCE_MAJOR,
+                    out: np.ndarray = None) -> np.ndarray:
+    """Return all-to-all.  z_rows: [R][cap][row] uint8.  Returns ret [R][T*k][row] uint8
+    (``out``, if given: a [R][T*k][row] uint8 array to write into).
     The expert-major layout needs the split table cnt [R][E]."""
     z_rows = _c(z_rows, np.uint8)
     R, cap, row = z_rows.shape
     if cnt is None:
         cnt = np.zeros((R, R * experts_per_rank), np.int32)
-    ret = np.zeros((R, T * k, row), np.uint8)
+    if out is None:
+        ret = np.zeros((R, T * k, row), np.uint8)
+    else:
+        assert out.shape == (R, T * k, row) and out.dtype == np.uint8 and out.flags.c_contiguous
+        ret = out
     rc = _load().oracle_return(R, T, k, experts_per_rank, row, cap, layout, _p(_c(cnt, np.int32)),
                                _p(_c(send_off, np.int32)), _p(_c(recv_off, np.int32)), _p(z_rows), _p(ret))
     if rc != 0:
@@ -139,14 +164,19 @@ def return_exchange(z_rows: np.ndarray, send_off: np.ndarray, recv_off: np.ndarr
     return ret
 
 
-def combine(ret: np.ndarray, pos: np.ndarray, gates: np.ndarray, dtype: int) -> np.ndarray:
-    """Gate-weighted combine.  ret: [R][T*k][H] float32/uint16; pos, gates: [R][T][k]."""
+def combine(ret: np.ndarray, pos: np.ndarray, gates: np.ndarray, dtype: int, out: np.ndarray = None) -> np.ndarray:
+    """Gate-weighted combine.  ret: [R][T*k][H] float32/uint16; pos, gates: [R][T][k].
+    ``out``, if given, is the [R][T][H] array to write into."""
     ret = np.ascontiguousarray(ret)
     pos = _c(pos, np.int32)
     gates = _c(gates, np.float32)
     R, T, k = pos.shape
     H = ret.shape[2]
-    y = np.zeros((R, T, H), ret.dtype)
+    if out is None:
+        y = np.zeros((R, T, H), ret.dtype)
+    else:
+        assert out.shape == (R, T, H) and out.dtype == ret.dtype and out.flags.c_contiguous
+        y = out
     rc = _load().oracle_combine(R, T, k, H, dtype, _p(pos), _p(gates), _p(ret), _p(y))
     if rc != 0:
         raise ValueError("oracle_combine rejected its arguments")
