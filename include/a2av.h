@@ -83,6 +83,8 @@ typedef struct a2av_context* a2av_handle_t;
 #define A2AV_ERR_INVALID (-1)   /* argument or configuration rejected */
 #define A2AV_ERR_NOMEM   (-2)   /* allocation failed (create; timing_begin on the host) */
 #define A2AV_ERR_HIP     (-3)   /* a HIP runtime call or launch failed */
+#define A2AV_ERR_SCRATCH (-4)   /* a2av_alltoallv_noalloc: the shape needs more scratch than
+                                   the library's fixed device array holds */
 
 /* device status bits, OR-ed into *status */
 #define A2AV_ST_EXPERT_RANGE  1u  /* an expert id was outside [0, E): that slot is dropped */
@@ -179,6 +181,32 @@ int a2av_combine(a2av_handle_t h, const void* expert_out, const float* gates, vo
  * Errors: A2AV_ERR_INVALID, A2AV_ERR_HIP. */
 int a2av_alltoallv(a2av_handle_t h, const void* send, const int32_t* send_counts, void* recv,
                    int32_t* recv_counts, int32_t* recv_offsets, uint32_t* status, void* stream);
+
+/* The bare collective of a2av_alltoallv with no handle and no allocation, for callers
+ * that cannot allocate device memory: code under hipGraph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The three tables the collective works with (send
+ * offsets [R][R+1], receive counts [R][R] and receive offsets [R][R+1]) live in one
+ * fixed array of A2AV_NOALLOC_SCRATCH_BYTES device bytes that the library holds on every
+ * GPU it runs on until the process ends; nothing else is used beyond the caller's
+ * buffers, and the call allocates nothing (no hipMalloc, no allocating library routine).
+ * cfg (host) gives the shape as for a2av_create: num_ranks R (at most
+ * A2AV_NOALLOC_MAX_RANKS), tokens_per_rank * top_k send rows per rank, hidden, dtype,
+ * recv_capacity_rows (0 = the worst case R * T * min(k, experts_per_rank));
+ * experts_per_rank and top_k are validated as for a2av_create; path and recv_layout
+ * are not used (the collective is always source-major).  send, send_counts, recv,
+ * recv_counts, recv_offsets, status and stream are as for a2av_alltoallv, and the
+ * results are identical to it.  The first call on a GPU looks up the array's device
+ * address (a runtime query); make that first call outside graph capture.  Every call
+ * on one GPU uses that GPU's one array: calls that overlap on one GPU (on different
+ * streams, or from different threads without stream order between them) race and give
+ * unspecified results.  Each call writes every table entry it reads, so nothing has to
+ * be cleared between calls.
+ * Errors: A2AV_ERR_INVALID (bad cfg or pointers), A2AV_ERR_SCRATCH (R over
+ * A2AV_NOALLOC_MAX_RANKS), A2AV_ERR_HIP; nothing is enqueued on an error. */
+#define A2AV_NOALLOC_MAX_RANKS 256
+#define A2AV_NOALLOC_SCRATCH_BYTES (1 << 20)
+int a2av_alltoallv_noalloc(const a2av_config_t* cfg, const void* send, const int32_t* send_counts, void* recv,
+                           int32_t* recv_counts, int32_t* recv_offsets, uint32_t* status, void* stream);
 
 /* Copy the position table of the latest dispatch into pos (device) [R][T][k]. */
 int a2av_copy_positions(a2av_handle_t h, int32_t* pos, void* stream);

@@ -16,6 +16,9 @@ OK = 0
 ERR_INVALID = -1
 ERR_NOMEM = -2
 ERR_HIP = -3
+ERR_SCRATCH = -4
+NOALLOC_MAX_RANKS = 256
+NOALLOC_SCRATCH_BYTES = 1 << 20
 ST_EXPERT_RANGE = 1
 ST_RECV_OVERFLOW = 2
 EXPERT_IDENTITY = 0
@@ -29,7 +32,7 @@ STAGE_NAMES = ("plan", "pack", "exchange", "return", "combine")
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liba2av.so")
 EXPORTS = ("a2av_create", "a2av_destroy", "a2av_workspace_bytes", "a2av_dispatch", "a2av_combine",
-           "a2av_alltoallv", "a2av_copy_positions", "a2av_copy_recv_expert_offsets", "a2av_copy_send_offsets",
+           "a2av_alltoallv", "a2av_alltoallv_noalloc", "a2av_copy_positions", "a2av_copy_recv_expert_offsets", "a2av_copy_send_offsets",
            "a2av_expert_apply",
            "a2av_route_step", "a2av_copy_reference", "a2av_timing_begin", "a2av_timing_end", "a2av_error_string")
 
@@ -68,6 +71,7 @@ def lib():
         L.a2av_dispatch.argtypes = [vp] * 9
         L.a2av_combine.argtypes = [vp] * 6
         L.a2av_alltoallv.argtypes = [vp] * 8
+        L.a2av_alltoallv_noalloc.argtypes = [ctypes.POINTER(Config)] + [vp] * 7
         L.a2av_copy_positions.argtypes = [vp, vp, vp]
         L.a2av_copy_send_offsets.argtypes = [vp, vp, vp]
         L.a2av_copy_recv_expert_offsets.argtypes = [vp, vp, vp]
@@ -147,6 +151,13 @@ def a2av_alltoallv(h, send, send_counts, recv, recv_counts, recv_offsets, status
     _check("a2av_alltoallv", lib().a2av_alltoallv(h, _ptr(send), _ptr(send_counts), _ptr(recv),
                                                   _ptr(recv_counts), _ptr(recv_offsets), _ptr(status),
                                                   _stream(stream)))
+
+
+def a2av_alltoallv_noalloc(cfg: Config, send, send_counts, recv, recv_counts, recv_offsets, status,
+                           stream=None) -> None:
+    _check("a2av_alltoallv_noalloc",
+           lib().a2av_alltoallv_noalloc(ctypes.byref(cfg), _ptr(send), _ptr(send_counts), _ptr(recv),
+                                        _ptr(recv_counts), _ptr(recv_offsets), _ptr(status), _stream(stream)))
 
 
 def a2av_copy_positions(h, pos, stream=None) -> None:

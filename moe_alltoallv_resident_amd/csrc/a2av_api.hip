@@ -4,6 +4,7 @@
 #include "../../include/a2av.h"
 #include "a2av_internal.h"
 
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -142,6 +143,64 @@ void drop_timing(a2av_context* h) {
 
 enum { kStagePlan = 0, kStagePack = 1, kStageExchange = 2, kStageReturn = 3, kStageCombine = 4 };
 
+// ---- the allocation-free bare collective -------------------------------------------
+// Its three tables (send offsets, receive counts, receive offsets) live in `scratch`, a
+// fixed device array each GPU holds for the life of the process.  Host code never uses
+// the array's name as an address (on the host it names a stand-in object): the device
+// address is looked up once per device with hipGetSymbolAddress and kept here.
+constexpr int kMaxDevices = 64;
+
+struct NoAllocLayout {
+    size_t send_off, recv_counts, recv_off, total;
+};
+
+NoAllocLayout noalloc_layout(int64_t R) {
+    NoAllocLayout m{};
+    size_t o = 0;
+    m.send_off = o;    o += align_up(sizeof(int32_t) * (size_t)R * (size_t)(R + 1));
+    m.recv_counts = o; o += align_up(sizeof(int32_t) * (size_t)R * (size_t)R);
+    m.recv_off = o;    o += align_up(sizeof(int32_t) * (size_t)R * (size_t)(R + 1));
+    m.total = o;
+    return m;
+}
+
+struct DeviceScratch {
+    void* ptr;    // device address of `scratch` on this device, null until looked up
+    int num_cu;
+};
+
+std::mutex g_scratch_mu;
+DeviceScratch g_scratch[kMaxDevices];
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[A2AV_NOALLOC_SCRATCH_BYTES];
+
+static_assert(A2AV_NOALLOC_MAX_RANKS <= a2av::kMaxRanks, "no-alloc rank limit");
+
+namespace {
+
+// This device's scratch address and CU count, looked up on its first call (with the
+// device current) and kept for every later call.
+int device_scratch(int dev, DeviceScratch* out) {
+    if (dev < 0 || dev >= kMaxDevices) return A2AV_ERR_INVALID;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    DeviceScratch& ds = g_scratch[dev];
+    if (!ds.ptr) {
+        void* p = nullptr;
+        int cus = 0;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return A2AV_ERR_HIP;
+        }
+        ds.num_cu = cus;
+        ds.ptr = p;
+    }
+    *out = ds;
+    return A2AV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -152,6 +211,7 @@ const char* a2av_error_string(int code) {
         case A2AV_ERR_INVALID: return "invalid argument or configuration";
         case A2AV_ERR_NOMEM: return "allocation failed";
         case A2AV_ERR_HIP: return "HIP runtime error";
+        case A2AV_ERR_SCRATCH: return "shape exceeds the no-alloc scratch array";
         default: return "unknown error code";
     }
 }
@@ -295,6 +355,40 @@ int a2av_alltoallv(a2av_handle_t h, const void* send, const int32_t* send_counts
     const a2av::Outputs out{nullptr, recv_counts, recv_offsets};
     if (a2av::launch_plan_from_counts(sh, h->tb, send_counts, status, st) != hipSuccess) return A2AV_ERR_HIP;
     if (a2av::launch_exchange(sh, h->tb, out, status, send, recv, false, true, vec, st) != hipSuccess)
+        return A2AV_ERR_HIP;
+    return A2AV_OK;
+}
+
+int a2av_alltoallv_noalloc(const a2av_config_t* cfg, const void* send, const int32_t* send_counts, void* recv,
+                           int32_t* recv_counts, int32_t* recv_offsets, uint32_t* status, void* stream) {
+    if (!cfg) return A2AV_ERR_INVALID;
+    a2av_config_t c = *cfg;
+    c.path = A2AV_PATH_STAGED;                 // not used by the bare collective
+    c.recv_layout = A2AV_LAYOUT_SOURCE_MAJOR;
+    Shape sh;
+    if (!make_shape(&c, &sh) || !send_counts || !status_ok(status)) return A2AV_ERR_INVALID;
+    if (sh.R > A2AV_NOALLOC_MAX_RANKS) return A2AV_ERR_SCRATCH;
+    const NoAllocLayout m = noalloc_layout(sh.R);
+    if (m.total > sizeof(scratch)) return A2AV_ERR_SCRATCH;
+    if (has_tokens(sh) && (!send || (sh.cap > 0 && !recv))) return A2AV_ERR_INVALID;
+    const void* ptrs[] = {send, recv};
+    const int vec = a2av::pick_vec_bytes(sh.row_bytes, ptrs, 2);
+    if (vec < min_vec(sh)) return A2AV_ERR_INVALID;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return A2AV_ERR_HIP;
+    DeviceScratch ds{};
+    const int rc = device_scratch(dev, &ds);
+    if (rc != A2AV_OK) return rc;
+    sh.num_cu = ds.num_cu;
+    char* base = static_cast<char*>(ds.ptr);
+    Tables tb{};                               // the collective touches only these three
+    tb.send_off = reinterpret_cast<int32_t*>(base + m.send_off);
+    tb.recv_counts = reinterpret_cast<int32_t*>(base + m.recv_counts);
+    tb.recv_off = reinterpret_cast<int32_t*>(base + m.recv_off);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const a2av::Outputs out{nullptr, recv_counts, recv_offsets};
+    if (a2av::launch_plan_from_counts(sh, tb, send_counts, status, st) != hipSuccess) return A2AV_ERR_HIP;
+    if (a2av::launch_exchange(sh, tb, out, status, send, recv, false, true, vec, st) != hipSuccess)
         return A2AV_ERR_HIP;
     return A2AV_OK;
 }

@@ -57,3 +57,20 @@ def test_workspace_bytes_counts_send_buffer_and_tables():
     # the direct path has no send buffer
     nd = a2av.a2av_workspace_bytes(a2av.make_config(R, T, H, a2av.BF16, epr, k, path=a2av.PATH_DIRECT))
     assert 0 < nd < 4 * 1024 * 1024
+
+
+def test_noalloc_collective_rejects_on_the_host():
+    """a2av_alltoallv_noalloc checks its shape before touching the GPU: an invalid
+    configuration or a missing counts pointer is A2AV_ERR_INVALID, more ranks than its
+    scratch array holds is A2AV_ERR_SCRATCH (pointers below are never dereferenced)."""
+    L = a2av.lib()
+    fake = ctypes.c_void_p(4096)
+    ok = dict(num_ranks=8, tokens_per_rank=4, hidden=64, dtype=a2av.BF16, experts_per_rank=1, top_k=1)
+    big = a2av.make_config(**dict(ok, num_ranks=a2av.NOALLOC_MAX_RANKS + 1))
+    assert L.a2av_alltoallv_noalloc(ctypes.byref(big), fake, fake, fake, None, None, fake, None) == a2av.ERR_SCRATCH
+    bad = a2av.make_config(**dict(ok, hidden=0))
+    assert L.a2av_alltoallv_noalloc(ctypes.byref(bad), fake, fake, fake, None, None, fake, None) == a2av.ERR_INVALID
+    good = a2av.make_config(**ok)
+    assert L.a2av_alltoallv_noalloc(ctypes.byref(good), fake, None, fake, None, None, fake, None) == a2av.ERR_INVALID
+    assert L.a2av_alltoallv_noalloc(None, fake, fake, fake, None, None, fake, None) == a2av.ERR_INVALID
+    assert "scratch" in a2av.error_string(a2av.ERR_SCRATCH)

@@ -1,0 +1,104 @@
+"""The allocation-free bare collective (a2av_alltoallv_noalloc) against the handle-based
+one (a2av_alltoallv), through the C ABI: identical receive rows, counts, offsets and
+status on consecutive calls that share the library's one scratch array, the second
+call smaller than the first; the largest rank count it accepts; shapes past its limit
+rejected on the host."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from moe_alltoallv_resident_amd import a2av
+from moe_alltoallv_resident_amd import workloads as W
+from tests.gpu_util import banner, host_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(R, T, H, seed):
+    """Sorted per-sender destinations, their counts, and bf16 token rows."""
+    rng = np.random.default_rng(seed)
+    dest = np.sort(rng.integers(0, R, size=(R, T)), axis=1).astype(np.int32)
+    if R > 2:
+        dest[1] = 0                                   # one sender, one peer
+        dest[2, :] = np.sort(rng.integers(0, 2, size=T))   # zero-length segments to the rest
+    counts = np.stack([np.bincount(dest[s], minlength=R) for s in range(R)]).astype(np.int32)
+    w = W.Workload("noalloc", R, T, H, W.BF16, 1, 1, "uniform", "softmax", 0, seed=seed)
+    return w, dest, counts, W.make_x(w)
+
+
+def _buffers(R, cap, H, fill):
+    recv = torch.full((R, cap, H), fill, dtype=torch.bfloat16, device="cuda")
+    rc = torch.full((R, R), -7, dtype=torch.int32, device="cuda")
+    ro = torch.full((R, R + 1), -7, dtype=torch.int32, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    return recv, rc, ro, st
+
+
+def _both(w, counts, x, bad_counts=None):
+    """Runs the handle-based and the no-alloc collective on the same inputs; returns the
+    host copies of (recv, recv_counts, recv_offsets, status) of each."""
+    R, T, H, cap = w.num_ranks, w.tokens_per_rank, w.hidden, w.capacity
+    cfg = a2av.make_config(R, T, H, W.BF16, 1, 1)
+    xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    sc = torch.from_numpy(counts if bad_counts is None else bad_counts).cuda()
+    outs = []
+    h = a2av.a2av_create(cfg)
+    b = _buffers(R, cap, H, 3.0)
+    a2av.a2av_alltoallv(h, xt, sc, *b)
+    torch.cuda.synchronize()
+    outs.append([host_bits(t) for t in b])
+    a2av.a2av_destroy(h)
+    b = _buffers(R, cap, H, 3.0)
+    a2av.a2av_alltoallv_noalloc(cfg, xt, sc, *b)
+    torch.cuda.synchronize()
+    outs.append([host_bits(t) for t in b])
+    return outs
+
+
+@pytest.mark.parametrize("shapes", [((8, 96, 640), (5, 40, 128)), ((256, 3, 64), (2, 7, 8))],
+                         ids=["8-then-5-ranks", "256-then-2-ranks"])
+def test_noalloc_matches_handle_collective_on_consecutive_calls(shapes):
+    for i, (R, T, H) in enumerate(shapes):
+        banner(f"no-alloc call {i}: R={R} T={T} H={H}")
+        w, dest, counts, x = _inputs(R, T, H, seed=11 + i)
+        ref_handle, got = _both(w, counts, x)
+        for a, b, name in zip(ref_handle, got, ("recv", "recv_counts", "recv_offsets", "status")):
+            assert np.array_equal(a, b), f"call {i}: {name} differs from a2av_alltoallv"
+        assert int(got[3][0]) == 0
+        # and both equal the oracle's exchange of the same rows
+        ref = oracle.dispatch(oracle.as_rows(x), dest[..., None], 1, w.capacity)
+        assert np.array_equal(got[1], ref["recv_counts"])
+        assert np.array_equal(got[2], ref["recv_off"])
+        want = ref["recv"].view(np.uint16).reshape(R, w.capacity, H)
+        for d in range(R):
+            n = int(ref["recv_off"][d, R])
+            assert np.array_equal(got[0][d, :n], want[d, :n]), f"call {i}: receive rows of rank {d}"
+
+
+def test_noalloc_flags_bad_counts_like_the_handle_collective():
+    w, dest, counts, x = _inputs(6, 40, 64, seed=5)
+    bad = counts.copy()
+    bad[1, 0] = -1                                     # negative
+    bad[3, 2] += w.tokens_per_rank                     # more rows than the sender holds
+    ref_handle, got = _both(w, counts, x, bad_counts=bad)
+    for a, b, name in zip(ref_handle, got, ("recv", "recv_counts", "recv_offsets", "status")):
+        assert np.array_equal(a, b), f"{name} differs from a2av_alltoallv"
+    assert int(got[3][0]) == a2av.ST_EXPERT_RANGE
+
+
+def test_noalloc_rejects_shapes_past_its_scratch_on_the_host():
+    R = a2av.NOALLOC_MAX_RANKS + 1
+    cfg = a2av.make_config(R, 2, 8, W.BF16, 1, 1)
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    counts = torch.zeros((R, R), dtype=torch.int32, device="cuda")
+    x = torch.zeros((R, 2, 8), dtype=torch.bfloat16, device="cuda")
+    recv = torch.zeros((R, 2 * R, 8), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(a2av.A2AVError) as e:
+        a2av.a2av_alltoallv_noalloc(cfg, x, counts, recv, None, None, st)
+    assert e.value.code == a2av.ERR_SCRATCH
+    with pytest.raises(a2av.A2AVError) as e:
+        a2av.a2av_alltoallv_noalloc(cfg, x, None, recv, None, None, st)
+    assert e.value.code == a2av.ERR_INVALID
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
