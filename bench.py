@@ -634,11 +634,13 @@ def traffic_json(workload, fetch_db, write_db):
     out = {"staged": {}, "direct": {}}
     for (name, gx), kib in fetch.items():
         base, targs = name.split("<")[0], [a.strip() for a in name.split("<", 1)[-1].rstrip(">").split(",")]
-        if base == "exchange_kernel":
+        if base == "exchange_kernel":        # <V, U, NT, REVERSE, FIRST, RPB>
             stage, direct = ("return" if targs[3] == "true" else "exchange"), False
-        elif base in ("pack_kernel", "pack_gather_kernel"):
+        elif base == "pack_kernel":          # <V, U, NT, NTS, DIRECT, RPB>
+            stage, direct = "pack", targs[4] == "true"
+        elif base == "pack_gather_kernel":   # <V, U, NT, DIRECT, RPB>
             stage, direct = "pack", targs[3] == "true"
-        elif base == "combine_kernel":
+        elif base == "combine_kernel":       # <B, DT, U, NT, DIRECT, PAIRS, RPB>
             stage, direct = "combine", targs[4] == "true"
         elif base in stage_of:
             stage, direct = stage_of[base], False
@@ -646,6 +648,8 @@ def traffic_json(workload, fetch_db, write_db):
             continue
         if stage is None or (name, gx) not in write:
             continue
+        if stage in out["direct" if direct else "staged"]:
+            raise RuntimeError(f"two kernels map to {stage}: run the counter passes with --paths staged,direct")
         out["direct" if direct else "staged"][stage] = {
             "read": int(round(kib * 1024.0 * read_factor)),
             "write": int(round(write[(name, gx)] * 1024.0 * write_factor)),

@@ -49,8 +49,8 @@ struct Outputs {
 // the row size and the alignment of every base address involved.
 int pick_vec_bytes(int64_t row_bytes, const void* const* ptrs, int nptrs);
 
-// Wavefronts per planning block for E experts (LDS holds (waves + 1) * E counters).
-int plan_waves(int32_t E);
+// Wavefronts per planning block for E experts when LDS holds (waves + rows) * E counters.
+int plan_waves(int32_t E, int rows);
 
 hipError_t launch_plan(const Shape& sh, const Tables& tb, const int32_t* ids, const Outputs& out,
                        uint32_t* status, hipStream_t st);
@@ -84,11 +84,11 @@ hipError_t launch_reference_copy(const void* src, void* dst, int64_t rows, int64
 hipError_t launch_route_step(const int32_t* ids_table, const float* gates_table, int32_t steps, int64_t n,
                              int32_t* counter, int32_t* ids, float* gates, hipStream_t st);
 
-// Dynamic LDS the planning kernel may use, and so the largest expert count: two rows
-// of E counters (one wavefront's and the totals) must fit.
+// Dynamic LDS the planning kernel may use, and so the largest expert count: three rows
+// of E counters (one wavefront's, the totals and the counts before a chunk) must fit.
 constexpr int32_t kPlanLdsBytes = 63 * 1024;
 constexpr int32_t kMaxExperts = 4096;
-static_assert(2 * 4 * kMaxExperts <= kPlanLdsBytes, "planning LDS budget");
+static_assert(3 * 4 * kMaxExperts <= kPlanLdsBytes, "planning LDS budget");
 constexpr int32_t kMaxRanks = 1024;
 constexpr int32_t kMaxTopK = 64;
 

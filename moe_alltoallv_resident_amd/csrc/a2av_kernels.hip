@@ -17,8 +17,8 @@
 //             reading the return buffer (staged) or the expert outputs in place (direct).
 // Everything but planning is a row copy or gather bound by HBM bandwidth: rows move as
 // 16-byte vectors, one 64-lane wavefront per row, with all of a row's loads issued
-// before its stores, stores non-temporal, loads non-temporal for buffers too large to
-// stay in cache.  Nothing here is a dense contraction, so no matrix-core instruction is
+// before its stores, stores non-temporal (but for the top-k pack's scattered stores at
+// streaming sizes), loads non-temporal for buffers too large to stay in cache.  Nothing here is a dense contraction, so no matrix-core instruction is
 // used.  Small steps (decode sizes) are bound by launches and dependent table reads
 // instead of bytes; there plan, tables and pack run as one launch in which every block
 // works from the routing ids (dispatch_small_kernel).
@@ -166,16 +166,22 @@ __device__ void write_recv_tables(const Shape& sh, const Tables& tb, const Outpu
 __host__ __device__ __forceinline__ int64_t table_blocks(int R) { return (R + kRowsPerBlock - 1) / kRowsPerBlock; }
 
 // ------------------------------------------------------------------------------------
-// plan: one block per rank (histogram, scans, stable positions, send offsets).
+// plan: histogram, scans, stable positions and send offsets of every rank.
 //
-// Positions are a stable counting sort by (expert, token, slot).  Each wavefront owns a
-// contiguous run of the rank's assignments and takes it in batches of S x 64, loading a
+// Positions are a stable counting sort by (expert, token, slot).  A rank's assignments
+// are cut into C chunks, one block each (C = 1 for a short rank).  Each wavefront of a
+// block owns a contiguous run of its chunk and takes it in batches of S x 64, loading a
 // whole batch before using it.  Lanes holding the same expert find each other with one
 // ballot per bit of the expert id (the AND of the matching ballots is the set of lanes
 // with an equal id); a lane's rank among them is the popcount of that set below it.  The
 // lowest such lane adds the group size to the wavefront's private LDS counter for that
-// expert, so no atomics are needed and the result does not depend on timing.  Counters
-// of all wavefronts are then scanned in (expert, wavefront) order into final bases.
+// expert, so no atomics decide a place and the result does not depend on timing.
+// Counters of all wavefronts are then scanned in (expert, wavefront) order into final
+// bases.  With C > 1 every block also counts the whole rank's histogram, and the part
+// of it in the chunks before its own, by LDS atomic increments (counts do not depend on
+// order): the rank's expert starts and its chunk's bases follow without waiting for any
+// other block.  (Measured at 8192 assignments per rank: one block per rank spends ~6 us
+// in the ballot matching alone, 16 wavefronts sharing one CU.)
 // ------------------------------------------------------------------------------------
 struct PlanArgs {
     Shape sh;
@@ -186,23 +192,45 @@ struct PlanArgs {
     bool inverse;   // also write inv (and dest = -1 for dropped slots) for the gather pack
 };
 
-// Planning of rank s by the whole block; lds holds (waves + 1) * E ints, wsum 17.
+// Planning of chunk c (of C) of rank s by the whole block; lds holds (waves + 1) * E
+// ints, (waves + 2) * E when C > 1; wsum 17.  Block c == 0 writes the rank's tables.
 template <int S>
-__device__ void plan_rank(const PlanArgs& a, int s, int* lds, int* wsum) {
+__device__ void plan_rank(const PlanArgs& a, int s, int c, int C, int* lds, int* wsum) {
     const Shape& sh = a.sh;
     const int E = sh.E, R = sh.R;
     const int tid = threadIdx.x, nt = blockDim.x, lane = lane_id(), w = tid / kWave, nw = nt / kWave;
     int* cw = lds;               // [nw][E] per-wavefront counters, later bases
-    int* tot = lds + nw * E;     // [E] per-expert totals, later exclusive offsets
+    int* tot = lds + nw * E;     // [E] per-expert totals of the rank, later exclusive offsets
+    int* bef = tot + E;          // [E] (C > 1) the rank's rows per expert in the chunks before c
 
-    for (int i = tid; i < nw * E; i += nt) cw[i] = 0;
+    for (int i = tid; i < (nw + (C > 1 ? 2 : 1)) * E; i += nt) lds[i] = 0;
     __syncthreads();
 
     const int64_t TK = sh.TK;
     const int32_t* ids = a.ids + (int64_t)s * TK;
     int32_t* pos = a.tb.pos + (int64_t)s * TK;
-    const int64_t chunk = ((TK + nw - 1) / nw + kWave - 1) / kWave * kWave;
-    const int64_t a0 = min(TK, (int64_t)w * chunk), a1 = min(TK, a0 + chunk);
+    const int64_t clen = ((TK + C - 1) / C + kWave - 1) / kWave * kWave;
+    const int64_t c0 = min(TK, (int64_t)c * clen), c1 = min(TK, c0 + clen);
+    if (C > 1) {
+        // the whole rank's histogram and that of the chunks before c; ids are read in
+        // rounds of kU per thread, all issued before any is used, at clamped indices
+        constexpr int kU = 8;
+        for (int64_t i0 = 0; i0 < TK; i0 += (int64_t)nt * kU) {
+            int ev[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) ev[u] = ids[min(i0 + (int64_t)u * nt + tid, TK - 1)];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int64_t i = i0 + (int64_t)u * nt + tid;
+                if (i < TK && (unsigned)ev[u] < (unsigned)E) {
+                    atomicAdd(&tot[ev[u]], 1);
+                    if (i < c0) atomicAdd(&bef[ev[u]], 1);
+                }
+            }
+        }
+    }
+    const int64_t chunk = ((c1 - c0 + nw - 1) / nw + kWave - 1) / kWave * kWave;
+    const int64_t a0 = min(c1, c0 + (int64_t)w * chunk), a1 = min(c1, a0 + chunk);
     const int64_t batch = (int64_t)S * kWave;
     const bool one_batch = a1 - a0 <= batch;
     int* mine = cw + w * E;
@@ -232,9 +260,9 @@ __device__ void plan_rank(const PlanArgs& a, int s, int* lds, int* wsum) {
             rk[u] = -1;
             if (in) {
                 const int r = __popcll(match & lanes_below(lane));
-                const int c = mine[e];
-                rk[u] = c + r;
-                if (r == 0) mine[e] = c + __popcll(match);
+                const int cnt = mine[e];
+                rk[u] = cnt + r;
+                if (r == 0) mine[e] = cnt + __popcll(match);
             }
             if (!one_batch && valid) pos[i] = rk[u];
         }
@@ -242,22 +270,29 @@ __device__ void plan_rank(const PlanArgs& a, int s, int* lds, int* wsum) {
     if (__ballot(bad) != 0 && lane == 0) atomicOr(a.status, 1u);
     __syncthreads();
 
-    // per expert: wavefront bases (exclusive over wavefronts) and the rank's count
+    // per expert: wavefront bases (exclusive over wavefronts); with one chunk, the
+    // rank's count is their sum
     for (int e = tid; e < E; e += nt) {
         int run = 0;
-        for (int v = 0; v < nw; ++v) { const int c = cw[v * E + e]; cw[v * E + e] = run; run += c; }
-        tot[e] = run;
-        a.tb.cnt[(int64_t)s * E + e] = run;
-        if (a.out.split) a.out.split[(int64_t)s * E + e] = run;
+        for (int v = 0; v < nw; ++v) { const int cc = cw[v * E + e]; cw[v * E + e] = run; run += cc; }
+        if (C == 1) tot[e] = run;
     }
     __syncthreads();
+    if (c == 0) {
+        for (int e = tid; e < E; e += nt) {
+            a.tb.cnt[(int64_t)s * E + e] = tot[e];
+            if (a.out.split) a.out.split[(int64_t)s * E + e] = tot[e];
+        }
+    }
     const int total = block_exclusive_scan(tot, E, wsum);   // tot[e] = first row of expert e
 
     // send segments: destination d holds experts d*epr .. d*epr+epr-1, which are
     // consecutive in the sorted order
-    for (int d = tid; d <= R; d += nt) a.tb.send_off[(int64_t)s * (R + 1) + d] = d < R ? tot[d * sh.epr] : total;
-    for (int e = tid; e <= E; e += nt) a.tb.eoff[(int64_t)s * (E + 1) + e] = e < E ? tot[e] : total;
-    for (int i = tid; i < nw * E; i += nt) cw[i] += tot[i % E];
+    if (c == 0) {
+        for (int d = tid; d <= R; d += nt) a.tb.send_off[(int64_t)s * (R + 1) + d] = d < R ? tot[d * sh.epr] : total;
+        for (int e = tid; e <= E; e += nt) a.tb.eoff[(int64_t)s * (E + 1) + e] = e < E ? tot[e] : total;
+    }
+    for (int i = tid; i < nw * E; i += nt) cw[i] += tot[i % E] + (C > 1 ? bef[i % E] : 0);
     __syncthreads();
 
     // pass 2: final positions; for the gather pack also the inverse (which assignment
@@ -286,11 +321,12 @@ __device__ void plan_rank(const PlanArgs& a, int s, int* lds, int* wsum) {
     }
 }
 
+// One block per (rank, chunk): block b plans chunk b % C of rank b / C.
 template <int S>
-__global__ void __launch_bounds__(1024) plan_kernel(PlanArgs a) {
+__global__ void __launch_bounds__(1024) plan_kernel(PlanArgs a, int C) {
     extern __shared__ int lds[];
     __shared__ int wsum[17];
-    plan_rank<S>(a, blockIdx.x, lds, wsum);
+    plan_rank<S>(a, blockIdx.x / C, blockIdx.x % C, C, lds, wsum);
 }
 
 // Expert-major receive places.  Receiver d's rows are grouped by local expert, then by
@@ -470,7 +506,8 @@ __device__ __forceinline__ int segment_of(const int32_t* so, int R, int64_t p, i
 
 // pack: row x[s][t] to its k places: the sender's send buffer (staged) or the
 // receivers' buffers (direct).  The blocks after the row blocks build the receive tables.
-template <typename V, int U, bool NT, bool DIRECT, int RPB>
+// NTS: non-temporal row stores (see launch_pack for when they are not).
+template <typename V, int U, bool NT, bool NTS, bool DIRECT, int RPB>
 __global__ void __launch_bounds__(RPB * kWave) pack_kernel(const V* __restrict__ x, V* __restrict__ dst, Shape sh,
                                                            Tables tb, Outputs out, uint32_t* status, Split sp) {
     const int lane = lane_id();
@@ -520,7 +557,7 @@ __global__ void __launch_bounds__(RPB * kWave) pack_kernel(const V* __restrict__
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int v = base + u * kWave + lane;
-                if (v < pc.v1) st<true>(row + v, r[u]);
+                if (v < pc.v1) st<NTS>(row + v, r[u]);
             }
         }
     }
@@ -728,7 +765,7 @@ __global__ void __launch_bounds__(kBlock) dispatch_small_kernel(const V* __restr
     const int R = sh.R;
     const int64_t A = (int64_t)R * sh.TK;
     if ((int)blockIdx.x < R) {                      // planning of one rank
-        plan_rank<1>(a, blockIdx.x, lds, wsum);
+        plan_rank<1>(a, blockIdx.x, 0, 1, lds, wsum);
         return;
     }
     if ((int)blockIdx.x < lead) {                   // receiver d's tables
@@ -1159,11 +1196,12 @@ __global__ void __launch_bounds__(1024) route_step_kernel(const int32_t* __restr
 inline unsigned row_blocks(int64_t rows) { return (unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock); }
 
 // Row loads are non-temporal once a kernel's rows are far larger than the caches (the
-// 256 MiB last-level cache); smaller steps keep them cacheable.  Row stores are always
-// non-temporal: no kernel reads back what it writes, and a kernel ends only after its
-// XCDs' L2s have written back every dirty line, which at decode sizes costs more than
-// the stores themselves (measured: non-temporal stores take about 1 us off each decode
-// launch that writes 10 MB).
+// 256 MiB last-level cache); smaller steps keep them cacheable.  Row stores are
+// non-temporal (the one exception is the top-k pack at streaming sizes, launch_pack): no
+// kernel reads back what it writes, and a kernel ends only after its XCDs' L2s have
+// written back every dirty line, which at decode sizes costs more than the stores
+// themselves (measured: non-temporal stores take about 1 us off each decode launch that
+// writes 10 MB).
 constexpr int64_t kStreamBytes = 256ll << 20;
 
 // At those sizes the path's copy kernels (pack, exchange, return) run at most two
@@ -1243,22 +1281,32 @@ int pick_vec_bytes(int64_t row_bytes, const void* const* ptrs, int nptrs) {
     return 0;
 }
 
-int plan_waves(int32_t E) { return std::max(1, std::min(16, (int)(kPlanLdsBytes / (4 * (int64_t)E)) - 1)); }
+int plan_waves(int32_t E, int rows) {
+    return std::max(1, std::min(16, (int)(kPlanLdsBytes / (4 * (int64_t)E)) - rows));
+}
+
+// Chunks per rank: one per 1024 assignments (one 64-assignment batch per wavefront of a
+// 16-wavefront block), at most 16, since every block of a rank counts all its ids.
+static int plan_chunks(int64_t TK) { return (int)std::max<int64_t>(1, std::min<int64_t>(16, (TK + 1023) / 1024)); }
 
 hipError_t launch_plan(const Shape& sh, const Tables& tb, const int32_t* ids, const Outputs& out, uint32_t* status,
                        hipStream_t st) {
-    // no more wavefronts than there are 64-assignment slices: idle ones would only add
-    // barrier and scan work
-    const int nw = (int)std::max<int64_t>(1, std::min<int64_t>(plan_waves(sh.E), (sh.TK + kWave - 1) / kWave));
-    const size_t lds = (size_t)(nw + 1) * sh.E * sizeof(int);
+    const int C = plan_chunks(sh.TK);
+    const int64_t clen = ((sh.TK + C - 1) / C + kWave - 1) / kWave * kWave;
+    const int rows = C > 1 ? 2 : 1;   // LDS rows of E counters beside the wavefronts'
+    // no more wavefronts than there are 64-assignment slices in a chunk: idle ones would
+    // only add barrier and scan work
+    const int nw = (int)std::max<int64_t>(1, std::min<int64_t>(plan_waves(sh.E, rows), (clen + kWave - 1) / kWave));
+    const size_t lds = (size_t)(nw + rows) * sh.E * sizeof(int);
     PlanArgs a{sh, tb, out, ids, status, gather_pack(sh)};
-    const int64_t per_wave = (sh.TK + nw - 1) / nw;
+    const int64_t per_wave = (clen + nw - 1) / nw;
     const int64_t slices = (per_wave + kWave - 1) / kWave;
-    if (slices <= 1) hipLaunchKernelGGL(plan_kernel<1>, dim3(sh.R), dim3(nw * kWave), lds, st, a);
-    else if (slices <= 2) hipLaunchKernelGGL(plan_kernel<2>, dim3(sh.R), dim3(nw * kWave), lds, st, a);
-    else if (slices <= 4) hipLaunchKernelGGL(plan_kernel<4>, dim3(sh.R), dim3(nw * kWave), lds, st, a);
-    else if (slices <= 8) hipLaunchKernelGGL(plan_kernel<8>, dim3(sh.R), dim3(nw * kWave), lds, st, a);
-    else hipLaunchKernelGGL(plan_kernel<16>, dim3(sh.R), dim3(nw * kWave), lds, st, a);
+    const dim3 grid((unsigned)(sh.R * C)), block(nw * kWave);
+    if (slices <= 1) hipLaunchKernelGGL(plan_kernel<1>, grid, block, lds, st, a, C);
+    else if (slices <= 2) hipLaunchKernelGGL(plan_kernel<2>, grid, block, lds, st, a, C);
+    else if (slices <= 4) hipLaunchKernelGGL(plan_kernel<4>, grid, block, lds, st, a, C);
+    else if (slices <= 8) hipLaunchKernelGGL(plan_kernel<8>, grid, block, lds, st, a, C);
+    else hipLaunchKernelGGL(plan_kernel<16>, grid, block, lds, st, a, C);
     return hipGetLastError();
 }
 
@@ -1298,6 +1346,14 @@ static hipError_t launch_pack_gather(const Shape& sh, const Tables& tb, const Ou
     });
 }
 
+// The top-k pack (k > 1) writes every token row to k places scattered over the experts'
+// runs.  At streaming sizes it loads and stores through the caches instead of
+// non-temporally: the L2s gather the scattered row stores before they go out (same-box
+// A/B at the top-8 shape, 16 x 2048 tokens of 14 KiB, receive capacity twice the mean:
+// staged pack 868 -> 788 us, direct 885 -> 791 us; cacheable stores alone 801 / 806 us).
+// Every other row kernel writes its rows in place order and is 7-10 % slower with
+// cacheable stores (prefill pack 218 -> 238 us, exchange 222 -> 235 us), so keeps
+// non-temporal ones.  Two blocks per CU, as the other streaming copies.
 hipError_t launch_pack(const Shape& sh, const Tables& tb, const Outputs& out, uint32_t* status, const void* x,
                        void* dst, bool direct, int vec, hipStream_t st) {
     if (gather_pack(sh)) return launch_pack_gather(sh, tb, out, status, x, dst, direct, vec, st);
@@ -1307,18 +1363,19 @@ hipError_t launch_pack(const Shape& sh, const Tables& tb, const Outputs& out, ui
     return with_vec(vec, [&](auto B) {
         using V = typename Vec<decltype(B)::value>::T;
         return with_unroll(sp.cv, [&](auto U) {
-            return with_nt(bytes, [&](auto NT) {
+            return with_nt(bytes, [&](auto STREAMING) {
                 constexpr int u = decltype(U)::value;
-                constexpr bool nt = decltype(NT)::value;
-                constexpr unsigned lds = nt ? kCopyLds : 0u;   // streaming: two blocks per CU
+                constexpr bool streaming = decltype(STREAMING)::value;
+                constexpr bool nts = !streaming;                      // streaming: cacheable stores
+                constexpr unsigned lds = streaming ? kCopyLds : 0u;   // streaming: two blocks per CU
                 constexpr int rpb = kRowsPerBlock;
                 const unsigned grid = (unsigned)((N * sp.cpr + rpb - 1) / rpb + (sh.R + rpb - 1) / rpb);
                 if (direct)
-                    hipLaunchKernelGGL((pack_kernel<V, u, nt, true, rpb>), dim3(grid), dim3(rpb * kWave), lds, st,
-                                       (const V*)x, (V*)dst, sh, tb, out, status, sp);
+                    hipLaunchKernelGGL((pack_kernel<V, u, false, nts, true, rpb>), dim3(grid), dim3(rpb * kWave), lds,
+                                       st, (const V*)x, (V*)dst, sh, tb, out, status, sp);
                 else
-                    hipLaunchKernelGGL((pack_kernel<V, u, nt, false, rpb>), dim3(grid), dim3(rpb * kWave), lds, st,
-                                       (const V*)x, (V*)dst, sh, tb, out, status, sp);
+                    hipLaunchKernelGGL((pack_kernel<V, u, false, nts, false, rpb>), dim3(grid), dim3(rpb * kWave), lds,
+                                       st, (const V*)x, (V*)dst, sh, tb, out, status, sp);
                 return hipGetLastError();
             });
         });

@@ -106,6 +106,10 @@ SMALL = [
     # more assignments per wavefront than its registers hold: planning in several batches
     ("wide", dict(num_ranks=2, tokens_per_rank=9000, hidden=16, experts_per_rank=8, top_k=2)),
     ("wide", dict(num_ranks=8, tokens_per_rank=2000, hidden=16, experts_per_rank=512, top_k=4)),
+    # ranks planned in 16 chunks of one wavefront each (4096 experts), each wavefront's run
+    # longer than one batch; and a ragged last chunk
+    ("wide", dict(num_ranks=2, tokens_per_rank=12000, hidden=8, experts_per_rank=2048, top_k=2)),
+    ("decode", dict(num_ranks=3, tokens_per_rank=5001, hidden=8)),
 ]
 
 
@@ -171,8 +175,8 @@ def test_every_token_routed_to_the_same_two_experts(path, layout, tokens):
     assert int(ref["recv_off"][2, 4]) == 4 * tokens * 2
 
 
-@pytest.mark.parametrize("tokens,hidden", [(24, 128), (16, 2048), (300, 128)],
-                         ids=["one-launch", "one-launch-split-count", "planned"])
+@pytest.mark.parametrize("tokens,hidden", [(24, 128), (16, 2048), (300, 128), (3000, 64)],
+                         ids=["one-launch", "one-launch-split-count", "planned", "planned-in-chunks"])
 @pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
 def test_out_of_range_ids_are_dropped_and_flagged(path, tokens, hidden):
     w = W.workload("wide", num_ranks=4, tokens_per_rank=tokens, hidden=hidden, experts_per_rank=4, top_k=2)
@@ -187,6 +191,8 @@ def test_out_of_range_ids_are_dropped_and_flagged(path, tokens, hidden):
     ids[1, 5, 1] = -(1 << 16)
     ids[0, 7, 0] = np.iinfo(np.int32).min
     ids[2, 4, 1] = np.iinfo(np.int32).max
+    if tokens > 1000:
+        ids[1, tokens // 2, 0] = -5          # in a middle chunk of a rank planned in chunks
     ref = _full_oracle_check(w, x, ids, gates, path)
     assert ref["status"] == oracle.ST_EXPERT_RANGE
 
