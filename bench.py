@@ -238,6 +238,13 @@ def main():
                                              "bytes_per_step", "stage_us", "roofline")}
             wide[label] = {"recv_capacity_rows_per_rank": cap,
                            "recv_bytes": ww.num_ranks * cap * ww.row_bytes, "paths": runs}
+        # the identity row copy of A rows of this shape, the achievable figure its kernels
+        # are compared with (as at the headline shape)
+        wsrc = torch.empty(ww.assignments * ww.row_bytes // 2, dtype=torch.int16, device="cuda")
+        wdst = torch.empty_like(wsrc)
+        wide["row_copy_reference_GBps"] = round(2 * ww.assignments * ww.row_bytes / (timed(
+            lambda: a2av.a2av_copy_reference(wsrc, wdst, ww.assignments, ww.row_bytes)) * 1e-3) / 1e9, 1)
+        del wsrc, wdst
         result["wide"] = wide
         del xwt, idwt, gwt
         torch.cuda.empty_cache()

@@ -25,7 +25,8 @@
  *     the handle was created; that GPU must be current at every call.  (host) marks
  *     host pointers.  A pointer to an array of zero elements (no tokens, or a
  *     receive capacity of 0) may be null.
- *   - `stream` is a hipStream_t passed as void*; NULL is the null stream.  All GPU work
+ *   - `stream` is a hipStream_t passed as void* (so that this header needs no HIP
+ *     header and plain C callers can include it); NULL is the null stream.  All GPU work
  *     is enqueued on it.  dispatch, combine and the harness calls never allocate,
  *     never synchronise and never copy to the host, so they can be captured in a
  *     hipGraph and replayed with routing that changes on the device.
@@ -121,17 +122,29 @@ typedef struct {
     int32_t recv_layout;        /* A2AV_LAYOUT_SOURCE_MAJOR or A2AV_LAYOUT_EXPERT_MAJOR */
 } a2av_config_t;
 
-/* Validate cfg (host) and allocate the handle's device workspace on the current GPU:
- * the send buffer (reused as the return buffer; staged path only), the position table
- * and the count/offset tables.  *out (host) receives the handle.  The workspace size is
- * a2av_workspace_bytes(cfg).  Errors: A2AV_ERR_INVALID, A2AV_ERR_NOMEM, A2AV_ERR_HIP. */
+/* Set-up, once per shape.  Under graph capture the buffers a collective touches are set
+ * up once, when the graph is captured, and must stay the same across replays, while the
+ * counts change inside them [abhik.ai page, section "Inference: small messages, unknown
+ * sizes"; qiguanping.github.io "NCCLX", section 7, figure 14]; so every device buffer
+ * the library itself needs is allocated here, at fixed addresses for the handle's life,
+ * and dispatch and combine allocate nothing.
+ *
+ * a2av_create: validate cfg (host) and allocate the handle's device workspace on the
+ * current GPU: the send buffer (reused as the return buffer; staged path only), the
+ * position table and the count/offset tables, zeroed.  *out (host) receives the handle
+ * (NULL on failure; nothing is left allocated).  The workspace size is
+ * a2av_workspace_bytes(cfg).  Errors: A2AV_ERR_INVALID (null pointer or a config outside
+ * the documented ranges), A2AV_ERR_NOMEM (device allocation failed), A2AV_ERR_HIP. */
 int a2av_create(const a2av_config_t* cfg, a2av_handle_t* out);
 
-/* Free the handle and its workspace.  The caller must have synchronised the streams
- * that used it.  NULL is accepted. */
+/* Free the handle and its workspace (the end of the set-up's lifetime).  The caller must
+ * have synchronised the streams that used it; work still in flight on it is undefined
+ * behaviour.  NULL is accepted (A2AV_OK).  Errors: A2AV_ERR_HIP if a free failed (the
+ * handle is released anyway). */
 int a2av_destroy(a2av_handle_t h);
 
-/* Device bytes a2av_create allocates for cfg, or -1 if cfg is invalid. */
+/* Device bytes a2av_create allocates for cfg (host), or -1 if cfg is invalid or null.
+ * Host-only: touches no GPU. */
 int64_t a2av_workspace_bytes(const a2av_config_t* cfg);
 
 /* Dispatch (the token sort and the all-to-allv, abhik.ai page, Figure 13):
