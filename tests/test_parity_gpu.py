@@ -275,7 +275,20 @@ def assert_combine_close_chunked(y_gpu, y_ref, dtype, what, chunk=4096):
 
 @pytest.mark.parametrize("name", ["decode", "prefill", "wide", "edge", "tiny"])
 def test_full_size_workload(name):
-    w = W.workload(name)
+    _check_at_size(W.workload(name))
+
+
+def test_streaming_sizes_with_two_byte_vectors():
+    # rows of 4094 bytes (2-byte vectors, 32 per lane) at sizes where every row kernel
+    # streams (655 MB per exchange): the non-temporal copies, the receive-order exchange
+    # and the top-k pack through the caches, with the narrowest vector type
+    w = W.workload("wide", num_ranks=4, tokens_per_rank=20000, hidden=2047, experts_per_rank=4, top_k=2)
+    assert w.assignments * w.row_bytes >= 256 << 20 and w.row_bytes % 4 == 2
+    _check_at_size(w)
+
+
+def _check_at_size(w: W.Workload):
+    name = w.name
     banner(f"full size {w.describe()} cap={w.capacity}")
     x, ids, gates = W.make_inputs(w)
     refs = {lay: oracle_tables(w, ids, lay) for lay in LAYOUTS}

@@ -102,3 +102,58 @@ def test_noalloc_rejects_shapes_past_its_scratch_on_the_host():
     assert e.value.code == a2av.ERR_INVALID
     torch.cuda.synchronize()
     assert int(st.item()) == 0
+
+
+def test_noalloc_replays_in_a_captured_graph_with_changing_counts():
+    """The point of the allocation-free form: captured in a graph (after its first call on
+    the device, which looks up its scratch address), it replays with counts a captured
+    device-side producer changes every replay, each replay equal to the handle-based
+    collective run eagerly on the same counts."""
+    R, T, H = 6, 48, 64
+    w = W.Workload("noalloc-graph", R, T, H, W.BF16, 1, 1, "uniform", "softmax", 0, seed=3)
+    x = W.make_x(w)
+    xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    cfg = a2av.make_config(R, T, H, W.BF16, 1, 1)
+    rng = np.random.default_rng(8)
+    tables = []
+    for _ in range(6):
+        dest = np.sort(rng.integers(0, R, size=(R, T)), axis=1)
+        tables.append(np.stack([np.bincount(dest[s], minlength=R) for s in range(R)]).astype(np.int32))
+    table_dev = torch.from_numpy(np.stack(tables)).cuda()
+    counts = torch.zeros((R, R), dtype=torch.int32, device="cuda")
+    step = torch.zeros(1, dtype=torch.int64, device="cuda")
+    recv, rc, ro, st = _buffers(R, w.capacity, H, 0.0)
+
+    def produce_and_exchange():
+        counts.copy_(table_dev.index_select(0, step).reshape(R, R))
+        a2av.a2av_alltoallv_noalloc(cfg, xt, counts, recv, rc, ro, st)
+
+    produce_and_exchange()                               # eager first call on this device
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        produce_and_exchange()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        produce_and_exchange()
+    h = a2av.a2av_create(cfg)
+    for i in (3, 1, 5, 0, 4):
+        banner(f"no-alloc graph replay with counts table {i}")
+        step.fill_(i)
+        recv.fill_(0.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [host_bits(t) for t in (recv, rc, ro)]
+        b = _buffers(R, w.capacity, H, 0.0)
+        a2av.a2av_alltoallv(h, xt, torch.from_numpy(tables[i]).cuda(), *b)
+        torch.cuda.synchronize()
+        want = [host_bits(t) for t in b[:3]]
+        for a_, b_, name in zip(got, want, ("recv", "recv_counts", "recv_offsets")):
+            assert np.array_equal(a_, b_), f"replay {i}: {name} differs from a2av_alltoallv"
+    assert int(st.item()) == 0
+    del g
+    a2av.a2av_destroy(h)
