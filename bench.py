@@ -96,6 +96,51 @@ def stage_bytes(w, direct):
     }
 
 
+def stage_rw_bytes(w, direct):
+    """(read, written) algorithmic bytes per launch of each row stage (stage_bytes split by
+    direction)."""
+    N, A, row = w.tokens, w.assignments, w.row_bytes
+    return {
+        "pack": (N * row + A * 4, A * row + (A * 8 if direct else 0)),
+        "exchange": (A * row, A * row),
+        "return": (A * row, A * row),
+        "combine": (A * row + A * (12 if direct else 8), N * row),
+    }
+
+
+def mix_ceiling(read, written, read_gbps, write_gbps):
+    """The fastest a kernel moving `read` + `written` bytes can go when reads alone stream
+    at read_gbps and writes alone at write_gbps."""
+    return (read + written) / (read / read_gbps + written / write_gbps)
+
+
+def annotate_ceilings(m, w, direct, read_gbps, write_gbps):
+    """Adds each row stage's mixed read/write ceiling and the fraction of it reached to a
+    time_path result (and to its roofline entry)."""
+    rw = stage_rw_bytes(w, direct)
+    fr = {}
+    for st, us in m["stage_us"].items():
+        if st not in rw:
+            continue
+        achieved = (rw[st][0] + rw[st][1]) / (us * 1e-6) / 1e9
+        fr[st] = round(achieved / mix_ceiling(rw[st][0], rw[st][1], read_gbps, write_gbps), 4)
+    m["stage_frac_of_mix_ceiling"] = fr
+    k = m["roofline"]["kernel"]
+    if k in rw:
+        m["roofline"]["mix_ceiling_GBps"] = round(mix_ceiling(rw[k][0], rw[k][1], read_gbps, write_gbps), 1)
+        m["roofline"]["frac_of_mix_ceiling"] = fr[k]
+
+
+def stream_ceilings(torch, a2av, nbytes, timed):
+    """Read-only and write-only stream bandwidth over nbytes (GB/s)."""
+    buf = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda")
+    out = torch.empty(a2av.STREAM_READ_OUT_BYTES // 4, dtype=torch.int32, device="cuda")
+    r = nbytes / (timed(lambda: a2av.a2av_stream_reference(buf, out, nbytes, a2av.STREAM_READ)) * 1e-3) / 1e9
+    wr = nbytes / (timed(lambda: a2av.a2av_stream_reference(None, buf, nbytes, a2av.STREAM_WRITE)) * 1e-3) / 1e9
+    del buf, out
+    return round(r, 1), round(wr, 1)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -186,6 +231,9 @@ def main():
     row_copy_gbps = 2 * ref_elems * 2 / (timed(lambda: a2av.a2av_copy_reference(src, dst, w.assignments, w.row_bytes))
                                          * 1e-3) / 1e9
     del src, dst
+    read_gbps, write_gbps = stream_ceilings(torch, a2av, w.assignments * w.row_bytes, timed)
+    for p in paths:
+        annotate_ceilings(measured[p], w, path_config(a2av, p)[0] == a2av.PATH_DIRECT, read_gbps, write_gbps)
 
     result = {
         "metric": "dispatch+combine µs/step and effective HBM GB/s (% of peak), 1 MI355X",
@@ -212,9 +260,11 @@ def main():
             "algorithmic_bytes_per_step": head["bytes_per_step"],
         },
         "stage_us": head["stage_us"],
+        "stage_frac_of_mix_ceiling": head["stage_frac_of_mix_ceiling"],
         "roofline": dict(head["roofline"], copy_reference_GBps=round(copy_gbps, 1),
                          row_copy_reference_GBps=round(row_copy_gbps, 1),
-                         frac_of_row_copy=round(head["roofline"]["achieved"] / row_copy_gbps, 4)),
+                         frac_of_row_copy=round(head["roofline"]["achieved"] / row_copy_gbps, 4),
+                         read_stream_GBps=read_gbps, write_stream_GBps=write_gbps),
     }
     for p in paths[1:]:
         result[f"{p.replace('-', '_')}_path"] = {k: v for k, v in measured[p].items()
@@ -230,12 +280,16 @@ def main():
         idwt, gwt = torch.from_numpy(idw).cuda(), torch.from_numpy(gw).cuda()
         worst = ww.num_ranks * ww.tokens_per_rank * min(ww.top_k, ww.experts_per_rank)
         wide = {"workload": ww.describe(), "steps": 10, "warmup": 3}
+        wide["read_stream_GBps"], wide["write_stream_GBps"] = stream_ceilings(
+            torch, a2av, ww.assignments * ww.row_bytes, timed)
         for label, cap in (("capacity_2x_mean", ww.capacity), ("capacity_worst_case", worst)):
             runs = {}
             for p in paths:
                 m = time_path(torch, a2av, ww, xwt, idwt, gwt, p, 10, 3, cap=cap)
+                annotate_ceilings(m, ww, path_config(a2av, p)[0] == a2av.PATH_DIRECT, wide["read_stream_GBps"],
+                                  wide["write_stream_GBps"])
                 runs[p] = {k: m[k] for k in ("us_per_step", "us_per_step_min", "GBps", "pct_hbm_peak",
-                                             "bytes_per_step", "stage_us", "roofline")}
+                                             "bytes_per_step", "stage_us", "stage_frac_of_mix_ceiling", "roofline")}
             wide[label] = {"recv_capacity_rows_per_rank": cap,
                            "recv_bytes": ww.num_ranks * cap * ww.row_bytes, "paths": runs}
         # the identity row copy of A rows of this shape, the achievable figure its kernels

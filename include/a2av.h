@@ -257,6 +257,21 @@ int a2av_route_step(const int32_t* ids_table, const float* gates_table, int32_t 
  * Errors: A2AV_ERR_INVALID, A2AV_ERR_HIP. */
 int a2av_copy_reference(const void* src, void* dst, int64_t rows, int64_t row_bytes, void* stream);
 
+/* Plain one-direction streams, for the bandwidth ceilings the path's kernels are read
+ * against (a kernel reading r bytes and writing w bytes cannot beat
+ * (r + w) / (r / read_bw + w / write_bw)).  bytes is a multiple of 16; pointers are
+ * 16-byte aligned device pointers.
+ *   A2AV_STREAM_READ: reads every byte of src once; dst receives
+ *     A2AV_STREAM_READ_OUT_BYTES bytes of 32-bit words whose XOR is the XOR of all of
+ *     src's 32-bit words (dst must hold that many bytes).
+ *   A2AV_STREAM_WRITE: writes all of dst: 16-byte vector i becomes the words
+ *     {i, i >> 32, 0x5A5A5A5A, ~i}; src is not used.
+ * Errors: A2AV_ERR_INVALID, A2AV_ERR_HIP. */
+#define A2AV_STREAM_READ  0
+#define A2AV_STREAM_WRITE 1
+#define A2AV_STREAM_READ_OUT_BYTES (1 << 20)
+int a2av_stream_reference(const void* src, void* dst, int64_t bytes, int32_t mode, void* stream);
+
 /* Stage timing with HIP events recorded between the library's kernels on the call's
  * stream.  a2av_timing_begin(h, max_calls), 1 <= max_calls <= A2AV_TIMING_MAX_CALLS,
  * creates events for up to max_calls

@@ -28,13 +28,16 @@ PATH_DIRECT = 1
 LAYOUT_SOURCE_MAJOR = 0
 LAYOUT_EXPERT_MAJOR = 1
 STAGES = 5
+STREAM_READ = 0
+STREAM_WRITE = 1
+STREAM_READ_OUT_BYTES = 1 << 20
 STAGE_NAMES = ("plan", "pack", "exchange", "return", "combine")
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liba2av.so")
 EXPORTS = ("a2av_create", "a2av_destroy", "a2av_workspace_bytes", "a2av_dispatch", "a2av_combine",
            "a2av_alltoallv", "a2av_alltoallv_noalloc", "a2av_copy_positions", "a2av_copy_recv_expert_offsets", "a2av_copy_send_offsets",
            "a2av_expert_apply",
-           "a2av_route_step", "a2av_copy_reference", "a2av_timing_begin", "a2av_timing_end", "a2av_error_string")
+           "a2av_route_step", "a2av_copy_reference", "a2av_stream_reference", "a2av_timing_begin", "a2av_timing_end", "a2av_error_string")
 
 TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16}
 
@@ -78,6 +81,7 @@ def lib():
         L.a2av_expert_apply.argtypes = [vp, vp, vp, i32, vp]
         L.a2av_route_step.argtypes = [vp, vp, i32, i64, vp, vp, vp, vp]
         L.a2av_copy_reference.argtypes = [vp, vp, i64, i64, vp]
+        L.a2av_stream_reference.argtypes = [vp, vp, i64, i32, vp]
         L.a2av_timing_begin.argtypes = [vp, i32]
         L.a2av_timing_end.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]
         L.a2av_error_string.argtypes = [ctypes.c_int]
@@ -184,6 +188,10 @@ def a2av_route_step(ids_table, gates_table, steps, n, counter, ids, gates, strea
 
 def a2av_copy_reference(src, dst, rows, row_bytes, stream=None) -> None:
     _check("a2av_copy_reference", lib().a2av_copy_reference(_ptr(src), _ptr(dst), rows, row_bytes, _stream(stream)))
+
+
+def a2av_stream_reference(src, dst, nbytes, mode, stream=None) -> None:
+    _check("a2av_stream_reference", lib().a2av_stream_reference(_ptr(src), _ptr(dst), nbytes, mode, _stream(stream)))
 
 
 def a2av_timing_begin(h, max_calls) -> None:

@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "liba2av.so")
-SOURCES = ["a2av_api.hip", "a2av_kernels.hip"]
+SOURCES = ["a2av_api.hip", "a2av_kernels.hip", "a2av_measure.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

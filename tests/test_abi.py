@@ -74,3 +74,13 @@ def test_noalloc_collective_rejects_on_the_host():
     assert L.a2av_alltoallv_noalloc(ctypes.byref(good), fake, None, fake, None, None, fake, None) == a2av.ERR_INVALID
     assert L.a2av_alltoallv_noalloc(None, fake, fake, fake, None, None, fake, None) == a2av.ERR_INVALID
     assert "scratch" in a2av.error_string(a2av.ERR_SCRATCH)
+
+
+def test_stream_reference_rejects_on_the_host():
+    L = a2av.lib()
+    fake = ctypes.c_void_p(4096)
+    assert L.a2av_stream_reference(fake, fake, 24, a2av.STREAM_READ, None) == a2av.ERR_INVALID     # not 16-byte units
+    assert L.a2av_stream_reference(fake, fake, 32, 7, None) == a2av.ERR_INVALID                    # no such mode
+    assert L.a2av_stream_reference(fake, None, 32, a2av.STREAM_WRITE, None) == a2av.ERR_INVALID    # no destination
+    assert L.a2av_stream_reference(None, fake, 32, a2av.STREAM_READ, None) == a2av.ERR_INVALID     # no source
+    assert L.a2av_stream_reference(fake, ctypes.c_void_p(4100), 32, a2av.STREAM_WRITE, None) == a2av.ERR_INVALID

@@ -105,3 +105,20 @@ def test_api_summary_counts_hip_calls_only(tmp_path, capsys):
     out = capsys.readouterr().out
     assert "| hipGraphLaunch | 3 |" in out and "| hipGetDevice | 2 |" in out
     assert "other" not in out
+
+
+def test_stage_read_write_split_sums_to_stage_bytes():
+    for name in BYTES:
+        w = W.workload(name)
+        for direct in (False, True):
+            total, rw = bench.stage_bytes(w, direct), bench.stage_rw_bytes(w, direct)
+            for st, (r, wr) in rw.items():
+                assert r + wr == total[st], (name, direct, st)
+
+
+def test_mix_ceiling():
+    # pure streams reach their own rate; an even mix the harmonic mean; more writes, lower
+    assert bench.mix_ceiling(10, 0, 7000.0, 5000.0) == 7000.0
+    assert bench.mix_ceiling(0, 10, 7000.0, 5000.0) == 5000.0
+    assert abs(bench.mix_ceiling(5, 5, 7000.0, 5000.0) - 2 / (1 / 7000.0 + 1 / 5000.0)) < 1e-9
+    assert bench.mix_ceiling(1, 8, 7000.0, 5000.0) < bench.mix_ceiling(8, 1, 7000.0, 5000.0)

@@ -267,6 +267,33 @@ def test_reference_copy(rows, row_bytes):
     assert L.a2av_copy_reference(None, None, 1, 24, stream) == a2av.ERR_INVALID
 
 
+@pytest.mark.parametrize("nbytes", [16, 16 * 1000, 3 << 20, 16 * 2_000_003])
+def test_stream_reference(nbytes):
+    """The measurement streams do what they claim: the write stream writes every vector's
+    pattern, the read stream's words XOR to the XOR of every word it read."""
+    n = nbytes // 16
+    dst = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda")
+    a2av.a2av_stream_reference(None, dst, nbytes, a2av.STREAM_WRITE)
+    torch.cuda.synchronize()
+    got = dst.cpu().numpy().view(np.uint32).reshape(n, 4)
+    i = np.arange(n, dtype=np.uint64)
+    assert np.array_equal(got[:, 0], (i & 0xFFFFFFFF).astype(np.uint32))
+    assert np.array_equal(got[:, 1], (i >> np.uint64(32)).astype(np.uint32))
+    assert np.all(got[:, 2] == 0x5A5A5A5A)
+    assert np.array_equal(got[:, 3], (~(i & 0xFFFFFFFF)).astype(np.uint32) & np.uint32(0xFFFFFFFF))
+    src = torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4,), dtype=torch.int32, device="cuda")
+    out = torch.full((a2av.STREAM_READ_OUT_BYTES // 4,), 7, dtype=torch.int32, device="cuda")
+    a2av.a2av_stream_reference(src, out, nbytes, a2av.STREAM_READ)
+    torch.cuda.synchronize()
+    want = np.bitwise_xor.reduce(src.cpu().numpy().view(np.uint32))
+    used = out.cpu().numpy().view(np.uint32)
+    # the kernel writes one word per thread of its grid (at most the whole output); words it
+    # did not write keep the fill value 7, which the XOR below must leave out
+    grid_words = min(4 * torch.cuda.get_device_properties(0).multi_processor_count * 256, used.size)
+    assert np.bitwise_xor.reduce(used[:grid_words]) == want
+    assert np.all(used[grid_words:] == 7)
+
+
 def test_bare_alltoallv_reads_counts_by_reference():
     """The counts are device data read when the collective executes: counts written by
     GPU work enqueued just before the call (no host synchronisation in between) are the
