@@ -1231,13 +1231,15 @@ hipError_t with_nt(int64_t bytes, F&& f) {
 constexpr int kWavesPerCu = 16;
 constexpr int kCombineWavesPerCu = 32;
 
-Split make_split(int64_t row_bytes, int vec, int64_t rows, int num_cu, int waves_per_cu = kWavesPerCu) {
+Split make_split(int64_t row_bytes, int vec, int64_t rows, int num_cu, int waves_per_cu = kWavesPerCu,
+                 int min_chunks = 1) {
     Split sp;
     sp.nvec = (int)(row_bytes / vec);
     int cpr = 1;
     if (rows > 0) {
         const int64_t target = (int64_t)num_cu * waves_per_cu;
-        cpr = (int)std::min<int64_t>((target + rows - 1) / rows, std::max(1, sp.nvec / kWave));
+        cpr = (int)std::max<int64_t>((target + rows - 1) / rows, min_chunks);
+        cpr = (int)std::min<int64_t>(cpr, std::max(1, sp.nvec / kWave));
         cpr = std::max(1, cpr);
     }
     int cv = (sp.nvec + cpr - 1) / cpr;
@@ -1248,6 +1250,20 @@ Split make_split(int64_t row_bytes, int vec, int64_t rows, int num_cu, int waves
 }
 
 inline unsigned piece_blocks(int64_t rows, const Split& sp) { return row_blocks(rows * sp.cpr); }
+
+// The exchanges (and the identity reference copy, which moves rows the same way) cut rows
+// of more than 12 vectors per lane in two at streaming sizes.  Same-box sweep, staged
+// exchange / return in us, whole rows -> two pieces: top-1 rows of 8 KiB 182 / 189 ->
+// 220 / 196, 10 KiB 221 / 213 -> 241 / 219, 12 KiB 266 / 267 -> 266 / 263, 14 KiB
+// 326 / 327 -> 309 / 313, 16 KiB 385 / 379 -> 363 / 367; top-8 (16 ranks x 1024 tokens)
+// the same way from 14 KiB on (return 646 -> 610 us at 14 KiB, 750 -> 721 at 16 KiB).
+// The packs keep whole rows (the top-8 pack was slower split).
+Split copy_split(int64_t row_bytes, int vec, int64_t rows, int num_cu) {
+    Split sp = make_split(row_bytes, vec, rows, num_cu);
+    if (sp.cpr == 1 && rows * row_bytes >= kStreamBytes && sp.nvec > 12 * kWave)
+        sp = make_split(row_bytes, vec, rows, num_cu, kWavesPerCu, 2);
+    return sp;
+}
 
 // Vectors per lane kept in flight: the smallest of 1, 2, 4, 8, 16 covering a chunk.
 template <typename F>
@@ -1417,7 +1433,7 @@ hipError_t launch_dispatch_small(const Shape& sh, const Tables& tb, const int32_
 hipError_t launch_exchange(const Shape& sh, const Tables& tb, const Outputs& out, uint32_t* status, const void* src,
                            void* dst, bool reverse, bool first, int vec, hipStream_t st) {
     const int64_t rows = (int64_t)sh.R * sh.TK;
-    const Split sp = make_split(sh.row_bytes, vec, rows, sh.num_cu);
+    const Split sp = copy_split(sh.row_bytes, vec, rows, sh.num_cu);
     const unsigned grid = (unsigned)((first ? table_blocks(sh.R) : 0) + piece_blocks(rows, sp));
     if (grid == 0) return hipSuccess;
     const int64_t bytes = rows * sh.row_bytes;
@@ -1452,8 +1468,12 @@ static hipError_t launch_combine_t(const Shape& sh, const Tables& tb, const void
                                    bool direct, hipStream_t st) {
     using V = typename Vec<B>::T;
     const int64_t N = (int64_t)sh.R * sh.T;
-    const Split sp = make_split(sh.row_bytes, B, N, sh.num_cu, kCombineWavesPerCu);
     const int64_t bytes = N * sh.row_bytes;
+    // at streaming sizes every row is cut in (at least) two pieces, one wavefront each:
+    // same-box A/B, prefill combine 227.5 -> 222.2 us staged and 229.9 -> 221.3 us direct,
+    // top-8 782 -> 738 us staged and 811 -> 766 us direct (four pieces: 775 / 799 us; the
+    // copy kernels split the same way were slower at prefill and are not split)
+    const Split sp = make_split(sh.row_bytes, B, N, sh.num_cu, kCombineWavesPerCu, bytes >= kStreamBytes ? 2 : 1);
     return with_unroll(sp.cv, [&](auto U) {
         return with_nt(bytes, [&](auto NT) {
             // keep float accumulators and the two slots' rows within a sane register
@@ -1536,7 +1556,7 @@ hipError_t launch_expert(const Shape& sh, const Tables& tb, const void* in, void
 hipError_t launch_reference_copy(const void* src, void* dst, int64_t rows, int64_t row_bytes, int num_cu,
                                  hipStream_t st) {
     if (rows == 0) return hipSuccess;
-    const Split sp = make_split(row_bytes, 16, rows, num_cu);
+    const Split sp = copy_split(row_bytes, 16, rows, num_cu);
     return with_unroll(sp.cv, [&](auto U) {
         return with_nt(rows * row_bytes, [&](auto NT) {
             constexpr bool nt = decltype(NT)::value;
