@@ -734,7 +734,7 @@ def traffic_json(workload, fetch_db, write_db):
 
 
 def _short_kernel_name(name):
-    base = name.replace("void ", "").replace("a2av::(anonymous namespace)::", "")
+    base = name.replace("void ", "").replace("a2av::(anonymous namespace)::", "").replace("(anonymous namespace)::", "")
     base = base.replace("unsigned int __vector(4)", "u32x4").replace("unsigned int __vector(2)", "u32x2")
     return base.split("(")[0]
 
