@@ -35,9 +35,9 @@ STAGE_NAMES = ("plan", "pack", "exchange", "return", "combine")
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liba2av.so")
 EXPORTS = ("a2av_create", "a2av_destroy", "a2av_workspace_bytes", "a2av_dispatch", "a2av_combine",
-           "a2av_alltoallv", "a2av_alltoallv_noalloc", "a2av_copy_positions", "a2av_copy_recv_expert_offsets", "a2av_copy_send_offsets",
-           "a2av_expert_apply",
-           "a2av_route_step", "a2av_copy_reference", "a2av_stream_reference", "a2av_timing_begin", "a2av_timing_end", "a2av_error_string")
+           "a2av_alltoallv", "a2av_alltoallv_noalloc", "a2av_copy_positions", "a2av_copy_recv_expert_offsets",
+           "a2av_copy_send_offsets", "a2av_expert_apply", "a2av_route_step", "a2av_copy_reference",
+           "a2av_stream_reference", "a2av_timing_begin", "a2av_timing_end", "a2av_error_string")
 
 TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16}
 
@@ -190,7 +190,18 @@ def a2av_copy_reference(src, dst, rows, row_bytes, stream=None) -> None:
     _check("a2av_copy_reference", lib().a2av_copy_reference(_ptr(src), _ptr(dst), rows, row_bytes, _stream(stream)))
 
 
+def _nbytes(t):
+    return t.numel() * t.element_size() if isinstance(t, torch.Tensor) else None
+
+
 def a2av_stream_reference(src, dst, nbytes, mode, stream=None) -> None:
+    # the kernels write a fixed-size result (read) or nbytes (write): short tensors are
+    # refused here rather than written past their end
+    need_dst = STREAM_READ_OUT_BYTES if mode == STREAM_READ else nbytes
+    if _nbytes(dst) is not None and _nbytes(dst) < need_dst:
+        raise ValueError(f"a2av_stream_reference: dst holds {_nbytes(dst)} bytes, needs {need_dst}")
+    if mode == STREAM_READ and _nbytes(src) is not None and _nbytes(src) < nbytes:
+        raise ValueError(f"a2av_stream_reference: src holds {_nbytes(src)} bytes, reads {nbytes}")
     _check("a2av_stream_reference", lib().a2av_stream_reference(_ptr(src), _ptr(dst), nbytes, mode, _stream(stream)))
 
 

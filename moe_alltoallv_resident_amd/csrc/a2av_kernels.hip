@@ -16,12 +16,13 @@
 //   combine   gate-weighted sum of each token's k expert rows, float32 accumulate,
 //             reading the return buffer (staged) or the expert outputs in place (direct).
 // Everything but planning is a row copy or gather bound by HBM bandwidth: rows move as
-// 16-byte vectors, one 64-lane wavefront per row, with all of a row's loads issued
-// before its stores, stores non-temporal (but for the top-k pack's scattered stores at
-// streaming sizes), loads non-temporal for buffers too large to stay in cache.  Nothing here is a dense contraction, so no matrix-core instruction is
-// used.  Small steps (decode sizes) are bound by launches and dependent table reads
-// instead of bytes; there plan, tables and pack run as one launch in which every block
-// works from the routing ids (dispatch_small_kernel).
+// 16-byte vectors, one 64-lane wavefront per row (or per piece of a row), with all of a
+// row's loads issued before its stores, stores non-temporal (but for the top-k pack's
+// scattered stores at streaming sizes), loads non-temporal for buffers too large to stay
+// in cache.  Nothing here is a dense contraction, so no matrix-core instruction is used.
+// Small steps (decode sizes) are bound by launches and dependent table reads instead of
+// bytes; there plan, tables and pack run as one launch in which every block works from
+// the routing ids (dispatch_small_kernel).
 #include "a2av_internal.h"
 
 #include <algorithm>
@@ -1471,8 +1472,8 @@ static hipError_t launch_combine_t(const Shape& sh, const Tables& tb, const void
     const int64_t bytes = N * sh.row_bytes;
     // at streaming sizes every row is cut in (at least) two pieces, one wavefront each:
     // same-box A/B, prefill combine 227.5 -> 222.2 us staged and 229.9 -> 221.3 us direct,
-    // top-8 782 -> 738 us staged and 811 -> 766 us direct (four pieces: 775 / 799 us; the
-    // copy kernels split the same way were slower at prefill and are not split)
+    // top-8 782 -> 738 us staged and 811 -> 766 us direct (four pieces: 775 / 799 us).
+    // The copy kernels cut only long rows (copy_split): shorter ones were slower cut.
     const Split sp = make_split(sh.row_bytes, B, N, sh.num_cu, kCombineWavesPerCu, bytes >= kStreamBytes ? 2 : 1);
     return with_unroll(sp.cv, [&](auto U) {
         return with_nt(bytes, [&](auto NT) {
