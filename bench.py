@@ -156,8 +156,8 @@ def main():
     ap.add_argument("--cpu-core", type=int, default=0, help=argparse.SUPPRESS)
     ap.add_argument("--traffic-json", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="turn rocprofv3 FETCH_SIZE and WRITE_SIZE databases of a run with --workload W "
-                         "--paths staged,direct into per-launch bytes and merge them into "
-                         "profiles/hbm_traffic.json under W (no GPU)")
+                         "--paths P (staged,direct or direct-expert-major; give the same --paths here) into "
+                         "per-launch bytes and merge them into profiles/hbm_traffic.json under W (no GPU)")
     ap.add_argument("--paths", default="staged,direct,direct-expert-major",
                     help="paths to time (staged, direct, staged-expert-major, direct-expert-major); "
                          "the first one gives the headline value")
@@ -172,7 +172,7 @@ def main():
         cpu_baseline_child(args.cpu_baseline_child, args.cpu_core)
         return
     if args.traffic_json:
-        traffic_json(args.workload, *args.traffic_json)
+        traffic_json(args.workload, *args.traffic_json, paths=args.paths)
         return
     if args.profile_summary:
         profile_summary(args.profile_summary)
@@ -402,7 +402,9 @@ def time_path(torch, a2av, w, xt, idt, gt, name, steps, warmup, trials=5, cap=No
         "roofline": {
             "bound": "hbm", "kernel": dom, "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic(w.name, path, dom), "bytes_per_launch": sb[dom],
+            # the counter passes run at the workload's own receive capacity
+            "traffic": measured_traffic(w.name, path, dom) if cap in (None, w.capacity) else None,
+            "bytes_per_launch": sb[dom],
             "us_per_launch": round(launch_ms[dom] * 1e3, 2),
         },
     }
@@ -666,11 +668,13 @@ def cpu_baseline_child(name, core, reps=3):
         "host_cpu": model, "host_threads_available": os.cpu_count()}), flush=True)
 
 
-def traffic_json(workload, fetch_db, write_db):
+def traffic_json(workload, fetch_db, write_db, paths="staged,direct", out_path=None):
     """Per-launch HBM bytes of the path's kernels from a FETCH_SIZE and a WRITE_SIZE pass
-    of `bench.py --workload W --paths staged,direct`, scaled by what the same counters read
-    for torch's device copy of A rows (the largest __amd_rocclr_copyBuffer launch, whose
-    bytes are known), merged into profiles/hbm_traffic.json under the workload."""
+    of `bench.py --workload W --paths P`, scaled by what the same counters read for
+    torch's device copy of A rows (the largest __amd_rocclr_copyBuffer launch, whose bytes
+    are known), merged into profiles/hbm_traffic.json under the workload.  P is
+    `staged,direct` or `direct-expert-major`: the kernels of the two layouts are the same
+    instances, so each layout needs passes of its own."""
     import sqlite3
 
     from moe_alltoallv_resident_amd import workloads as W
@@ -692,7 +696,12 @@ def traffic_json(workload, fetch_db, write_db):
     write_factor = copy_bytes / (write[big] * 1024.0)
     stage_of = {"plan_kernel": None, "pack_kernel": "pack", "pack_gather_kernel": "pack",
                 "exchange_recv_order_kernel": "exchange", "combine_kernel": "combine"}
-    out = {"staged": {}, "direct": {}}
+    names = [p.strip() for p in paths.split(",") if p.strip()]
+    expert_major = all(p.endswith("-expert-major") for p in names)
+    if not expert_major and any(p.endswith("-expert-major") for p in names):
+        raise RuntimeError("take the counters of the source-major and expert-major paths in separate passes")
+    suffix = "-expert-major" if expert_major else ""
+    out = {}
     for (name, gx), kib in fetch.items():
         base, targs = name.split("<")[0], [a.strip() for a in name.split("<", 1)[-1].rstrip(">").split(",")]
         if base == "exchange_kernel":        # <V, U, NT, REVERSE, FIRST, RPB>
@@ -709,13 +718,14 @@ def traffic_json(workload, fetch_db, write_db):
             continue
         if stage is None or (name, gx) not in write:
             continue
-        if stage in out["direct" if direct else "staged"]:
-            raise RuntimeError(f"two kernels map to {stage}: run the counter passes with --paths staged,direct")
-        out["direct" if direct else "staged"][stage] = {
+        key = ("direct" if direct else "staged") + suffix
+        if stage in out.setdefault(key, {}):
+            raise RuntimeError(f"two kernels map to {key} {stage}: one layout per counter pass")
+        out[key][stage] = {
             "read": int(round(kib * 1024.0 * read_factor)),
             "write": int(round(write[(name, gx)] * 1024.0 * write_factor)),
             "kernel": name, "grid_x": gx}
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    path = out_path or os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)
@@ -724,10 +734,11 @@ def traffic_json(workload, fetch_db, write_db):
     sha = kernel_source_sha256()
     if rec.get("kernel_source_sha256") != sha:
         rec = {"kernel_source_sha256": sha, "workloads": {}}
-    rec.setdefault("workloads", {})[workload] = {
-        "calibration": {"copy_bytes_each_way": copy_bytes, "fetch_kib": fetch[big], "write_kib": write[big],
-                        "read_factor": round(read_factor, 5), "write_factor": round(write_factor, 5)},
-        "per_launch_bytes": out}
+    wrec = rec.setdefault("workloads", {}).setdefault(workload, {})
+    wrec["calibration" + suffix.replace("-", "_")] = {
+        "copy_bytes_each_way": copy_bytes, "fetch_kib": fetch[big], "write_kib": write[big],
+        "read_factor": round(read_factor, 5), "write_factor": round(write_factor, 5)}
+    wrec.setdefault("per_launch_bytes", {}).update(out)
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec["workloads"][workload], indent=1))

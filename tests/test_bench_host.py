@@ -1,6 +1,7 @@
 """Host-side logic of bench.py (no GPU): the algorithmic byte counts every bandwidth
 figure divides by, the one-GPU guard, and the profile summaries read from rocprofv3
 databases."""
+import json
 import os
 import sqlite3
 import subprocess
@@ -122,3 +123,61 @@ def test_mix_ceiling():
     assert bench.mix_ceiling(0, 10, 7000.0, 5000.0) == 5000.0
     assert abs(bench.mix_ceiling(5, 5, 7000.0, 5000.0) - 2 / (1 / 7000.0 + 1 / 5000.0)) < 1e-9
     assert bench.mix_ceiling(1, 8, 7000.0, 5000.0) < bench.mix_ceiling(8, 1, 7000.0, 5000.0)
+
+
+def _counter_db(path, counter, rows):
+    c = sqlite3.connect(path)
+    c.execute("create table counters_collection (kernel_name text, grid_size_x int, counter_name text, value real)")
+    c.executemany("insert into counters_collection values (?, ?, ?, ?)",
+                  [(name, gx, counter, v) for name, gx, v in rows])
+    c.commit()
+    c.close()
+
+
+_NS = "void a2av::(anonymous namespace)::"
+_COPY = "__amd_rocclr_copyBuffer(int)"
+
+
+def test_traffic_json_scales_by_the_copy_and_keeps_each_layout(tmp_path, capsys):
+    w = W.workload("tiny")
+    copy = w.assignments * w.row_bytes                    # bytes each way of the calibration copy
+    out = str(tmp_path / "traffic.json")
+    # the copy's FETCH_SIZE reads half its bytes (reads x2), WRITE_SIZE all of them (x1)
+    src = [(_COPY, 64, copy / 2048.0), (_COPY, 32, 1.0),  # the largest copy is the calibration
+           (_NS + "pack_gather_kernel<unsigned int __vector(4), 1, false, false, 4>(int)", 4096, 10.0),
+           (_NS + "pack_gather_kernel<unsigned int __vector(4), 1, false, true, 4>(int)", 4096, 20.0),
+           (_NS + "exchange_recv_order_kernel<unsigned int __vector(4), 1, false, 4>(int)", 2048, 30.0),
+           (_NS + "exchange_kernel<unsigned int __vector(4), 1, false, true, false, 4>(int)", 2048, 40.0),
+           (_NS + "combine_kernel<16, 0, 1, false, false, false, 4>(int)", 1024, 50.0),
+           (_NS + "combine_kernel<16, 0, 1, false, true, false, 4>(int)", 1024, 60.0),
+           (_NS + "plan_kernel<1>(int)", 4096, 70.0)]
+    fetch, write = str(tmp_path / "f.db"), str(tmp_path / "w.db")
+    _counter_db(fetch, "FETCH_SIZE", src)
+    _counter_db(write, "WRITE_SIZE", [(n, g, v * 2 if n.startswith(_COPY) else v) for n, g, v in src])
+    bench.traffic_json("tiny", fetch, write, "staged,direct", out_path=out)
+    rec = json.load(open(out))
+    per = rec["workloads"]["tiny"]["per_launch_bytes"]
+    assert sorted(per) == ["direct", "staged"]
+    assert sorted(per["staged"]) == ["combine", "exchange", "pack", "return"]
+    assert sorted(per["direct"]) == ["combine", "pack"]
+    assert per["staged"]["pack"]["read"] == 2 * 10 * 1024 and per["staged"]["pack"]["write"] == 10 * 1024
+    assert per["direct"]["combine"]["read"] == 2 * 60 * 1024
+    assert per["staged"]["return"]["write"] == 40 * 1024
+    cal = rec["workloads"]["tiny"]["calibration"]
+    assert cal["read_factor"] == 2.0 and cal["write_factor"] == 1.0
+    # an expert-major pass lands beside the source-major figures, not over them
+    _counter_db(str(tmp_path / "f2.db"), "FETCH_SIZE", src[:2] + [src[3], src[7]])
+    _counter_db(str(tmp_path / "w2.db"), "WRITE_SIZE", [(n, g, v * 2 if n.startswith(_COPY) else v)
+                                                        for n, g, v in src[:2] + [src[3], src[7]]])
+    bench.traffic_json("tiny", str(tmp_path / "f2.db"), str(tmp_path / "w2.db"), "direct-expert-major",
+                       out_path=out)
+    rec = json.load(open(out))
+    per = rec["workloads"]["tiny"]["per_launch_bytes"]
+    assert sorted(per) == ["direct", "direct-expert-major", "staged"]
+    assert per["direct-expert-major"]["pack"]["read"] == 2 * 20 * 1024
+    assert per["direct"]["combine"]["read"] == 2 * 60 * 1024
+    assert "calibration_expert_major" in rec["workloads"]["tiny"]
+    # one layout per pass: both at once cannot be told apart
+    with pytest.raises(RuntimeError):
+        bench.traffic_json("tiny", fetch, write, "direct,direct-expert-major", out_path=out)
+    capsys.readouterr()
