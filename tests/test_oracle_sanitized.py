@@ -1,8 +1,9 @@
 """The oracle's pins under AddressSanitizer and UndefinedBehaviorSanitizer (no GPU).
 
 The oracle source is built a second time with both sanitizers, every finding fatal
-(oracle/build.py), and the pin suite and the golden test run in a child process that
-has the sanitizer runtime preloaded and loads that build.  A second child passes the
+(oracle/build.py), and the pin suite, the property-based pins and the golden test run
+in a child process that has the sanitizer runtime preloaded and loads that build.  A
+second child passes the
 sanitized oracle a receive buffer one row short and must be stopped by the sanitizer,
 which shows the checking layer is live.  Checking communication logic on CPUs before
 it meets the hardware follows abhik.ai "Collective Communication for 100k+ GPUs",
@@ -46,7 +47,8 @@ def test_sanitized_oracle_is_the_one_loaded(sanitized_env):
 
 def test_oracle_pins_pass_under_address_and_undefined_behaviour_sanitizers(sanitized_env):
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        "tests/test_oracle_pins.py", "tests/test_golden.py"],
+                        "tests/test_oracle_pins.py", "tests/test_oracle_properties.py",
+                        "tests/test_golden.py"],
                        cwd=ROOT, env=sanitized_env, capture_output=True, text=True, timeout=900)
     assert r.returncode == 0, (r.stdout[-3000:], r.stderr[-3000:])
     assert "passed" in r.stdout and "failed" not in r.stdout
