@@ -147,6 +147,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill")
+    ap.add_argument("--recv-capacity", type=int, default=0, metavar="ROWS",
+                    help="receive capacity per rank for the headline workload (0: the workload's own); "
+                         "for counter passes at another capacity")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode-graph", action="store_true")
     ap.add_argument("--no-wide", action="store_true",
@@ -197,7 +200,7 @@ def main():
     if args.decode_graph_only:
         print(json.dumps(decode_graph(np, torch, a2av, W, paths[0], replays=args.decode_graph_only)), flush=True)
         return
-    w = W.workload(args.workload)
+    w = W.workload(args.workload, **({"recv_capacity_rows": args.recv_capacity} if args.recv_capacity else {}))
     log(f"workload {w.describe()}; generating inputs")
     x, ids, gates = W.make_inputs(w)
     if w.dtype == W.BF16:
@@ -328,9 +331,11 @@ def time_path(torch, a2av, w, xt, idt, gt, name, steps, warmup, trials=5, cap=No
     dispatch+combine pairs (the headline: median trial, launch gaps included, no event
     between kernels; the minimum beside it), and `steps` full steps with the expert
     stand-in between them.  `cap` overrides the workload's receive capacity."""
+    from moe_alltoallv_resident_amd import workloads as W
     path_id, layout = path_config(a2av, name)
     direct = path_id == a2av.PATH_DIRECT
     path = name
+    at_own_capacity = (w.capacity if cap is None else cap) == W.workload(w.name).capacity
     s = a2av.Session(w.num_ranks, w.tokens_per_rank, w.hidden, w.dtype, w.experts_per_rank, w.top_k,
                      w.recv_capacity_rows if cap is None else cap, path=path_id, recv_layout=layout)
     y = torch.empty_like(xt)
@@ -403,7 +408,7 @@ def time_path(torch, a2av, w, xt, idt, gt, name, steps, warmup, trials=5, cap=No
             "bound": "hbm", "kernel": dom, "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
             # the counter passes run at the workload's own receive capacity
-            "traffic": measured_traffic(w.name, path, dom) if cap in (None, w.capacity) else None,
+            "traffic": measured_traffic(w.name, path, dom) if at_own_capacity else None,
             "bytes_per_launch": sb[dom],
             "us_per_launch": round(launch_ms[dom] * 1e3, 2),
         },
