@@ -35,9 +35,9 @@
  *     enqueued).
  *   - Problems only the GPU can see (an expert id outside [0, E), a rank receiving
  *     more rows than its capacity) OR bits into the caller's device word `*status`
- *     (sticky; the library never clears or reads it; it must be 4-byte aligned).  No write ever goes out of
- *     bounds: a dropped assignment is not sent, a row past the capacity is not
- *     written, and either adds zero to the combine.  Counts stay true.
+ *     (sticky; the library never clears or reads it; it must be 4-byte aligned).  No
+ *     write ever goes out of bounds: a dropped assignment is not sent, a row past the
+ *     capacity is not written, and either adds zero to the combine.  Counts stay true.
  *   - A handle serves one dispatch/combine pair at a time: combine uses the routing
  *     of the most recent dispatch on the same handle, in stream order.  Handles are
  *     not thread-safe.
@@ -187,10 +187,10 @@ int a2av_combine(a2av_handle_t h, const void* expert_out, const float* gates, vo
  * send_counts[s][0..d-1]; send_counts (device) [R][R] ([src][dst]) is read when the
  * kernels run, so it may be written by earlier work on the stream.  Rows land in recv
  * (device) [R][cap][H] source-major; recv_counts / recv_offsets (device, optional) as
- * for dispatch (always source-major).  A negative count, or counts of one sender summing past T*k, set
- * A2AV_ST_EXPERT_RANGE and that sender's counts are taken as 0.  It replaces the
- * handle's routing state: a2av_combine and a2av_expert_apply after it return
- * A2AV_ERR_INVALID until the next a2av_dispatch.
+ * for dispatch (always source-major).  A negative count, or counts of one sender
+ * summing past T*k, set A2AV_ST_EXPERT_RANGE and that sender's counts are taken as 0.
+ * It replaces the handle's routing state: a2av_combine and a2av_expert_apply after it
+ * return A2AV_ERR_INVALID until the next a2av_dispatch.
  * Errors: A2AV_ERR_INVALID, A2AV_ERR_HIP. */
 int a2av_alltoallv(a2av_handle_t h, const void* send, const int32_t* send_counts, void* recv,
                    int32_t* recv_counts, int32_t* recv_offsets, uint32_t* status, void* stream);
@@ -274,9 +274,8 @@ int a2av_stream_reference(const void* src, void* dst, int64_t bytes, int32_t mod
 
 /* Stage timing with HIP events recorded between the library's kernels on the call's
  * stream.  a2av_timing_begin(h, max_calls), 1 <= max_calls <= A2AV_TIMING_MAX_CALLS,
- * creates events for up to max_calls
- * dispatch and max_calls combine calls (host-side event objects only; no device
- * memory); later calls record until the budget is used.  a2av_timing_end waits for
+ * creates events for up to max_calls dispatch and max_calls combine calls (host-side
+ * event objects only; no device memory); later calls record until the budget is used.  a2av_timing_end waits for
  * the recorded events, writes per-stage sums of milliseconds into ms_sum (host)
  * [A2AV_STAGES] and the number of timed launches per stage into launches (host)
  * [A2AV_STAGES], and releases the events.  Stages: 0 plan (histogram + scans), 1 pack,
