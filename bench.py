@@ -310,6 +310,12 @@ def main():
         result["graph_kernel_node_us"] = graph_kernel_node_us(torch, a2av)
         result["decode_graph"] = {p: decode_graph(np, torch, a2av, W, p) for p in paths}
         result["edge_graph"] = {p: decode_graph(np, torch, a2av, W, p, workload="edge") for p in paths}
+        # decode latency against batch size: tokens per rank from 16 to 1024 at the decode
+        # shape, zero-copy path (the one-launch dispatch up to 512 tokens per rank here)
+        sweep_path = "direct" if "direct" in paths else paths[0]
+        result["decode_sweep"] = {"path": sweep_path, "workload": W.workload("decode").describe(), "points": [
+            decode_graph(np, torch, a2av, W, sweep_path, steps=50, over={"tokens_per_rank": t}, light=True)
+            for t in (16, 32, 64, 128, 256, 384, 512, 768, 1024)]}
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w)
@@ -415,7 +421,8 @@ def time_path(torch, a2av, w, xt, idt, gt, name, steps, warmup, trials=5, cap=No
     }
 
 
-def decode_graph(np, torch, a2av, W, path, workload="decode", steps=100, per_graph=10, replays=None):
+def decode_graph(np, torch, a2av, W, path, workload="decode", steps=100, per_graph=10, replays=None, over=None,
+                 light=False):
     """A latency-bound shape captured in hipGraphs and replayed with routing that changes
     on the device every step (router stand-in -> dispatch -> expert stand-in -> combine),
     one event pair around all replays and no host synchronisation between them.
@@ -427,8 +434,9 @@ def decode_graph(np, torch, a2av, W, path, workload="decode", steps=100, per_gra
     another kernel has just written, as it would after a real expert.  The flushed
     variant writes 512 MiB before every step, so each step starts with its inputs out of
     the 256 MiB last-level cache.  With `replays`, only the one-step graph is captured
-    and replayed that many times (for API tracing)."""
-    w = W.workload(workload)
+    and replayed that many times (for API tracing).  `over` replaces workload fields;
+    `light` keeps only the dispatch, combine and reference-copy figures."""
+    w = W.workload(workload, **(over or {}))
     log(f"graph latency ({path}): {w.describe()}, {steps} steps")
     x = W.make_x(w)
     n = w.tokens * w.top_k
@@ -529,6 +537,21 @@ def decode_graph(np, torch, a2av, W, path, workload="decode", steps=100, per_gra
     t_route_dispatch = us_per_step(route_dispatch, per_graph, steps)
     t_route_dispatch_expert = us_per_step(route_dispatch_expert, per_graph, steps)
     t_copy = us_per_step(reference_copy, per_graph, steps, routed=False)
+    if light:
+        ok = int(s.status.item()) == 0
+        t_dispatch, t_combine = t_route_dispatch - t_route, t_full - t_route_dispatch_expert
+        del ref_src, ref_dst
+        s.close()
+        torch.cuda.empty_cache()
+        return {"tokens_per_rank": w.tokens_per_rank, "assignments": w.assignments,
+                # the library's rule for dispatching in one launch (include/a2av.h)
+                "one_launch_dispatch": bool(w.tokens_per_rank > 0 and w.tokens_per_rank * w.top_k <= 1024
+                                            and w.num_experts <= 1024
+                                            and (w.assignments <= 2048 or (w.assignments <= 4096 and (
+                                                path_id == a2av.PATH_STAGED or w.top_k == 1)))),
+                "us_dispatch": round(t_dispatch, 2), "us_combine": round(t_combine, 2),
+                "us_reference_copy": round(t_copy, 2), "bytes_dispatch": (w.tokens + w.assignments) * w.row_bytes,
+                "status_ok": ok}
     t_one = us_per_step(full, 1, steps)
     flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     t_full_f = us_per_step(flushed(full), per_graph, steps)

@@ -297,7 +297,7 @@ int a2av_dispatch(a2av_handle_t h, const void* x, const int32_t* topk_ids, void*
     const a2av::Tables& tb = h->tb;
     void* dst = h->direct ? recv : h->send_buf;
     int rc;
-    if (a2av::small_dispatch(sh)) {
+    if (a2av::small_dispatch(sh, h->direct)) {
         rc = launch_timed(h, kStagePack, st, [&] {
             return a2av::launch_dispatch_small(sh, tb, topk_ids, out, status, x, dst, h->direct, vec, st);
         });

@@ -58,7 +58,7 @@ hipError_t launch_plan_from_counts(const Shape& sh, const Tables& tb, const int3
                                    uint32_t* status, hipStream_t st);
 // Small steps (decode sizes): planning, receiver tables (and expert-major places) and
 // the pack in one launch in which every block works from the ids alone.
-bool small_dispatch(const Shape& sh);
+bool small_dispatch(const Shape& sh, bool direct);
 hipError_t launch_dispatch_small(const Shape& sh, const Tables& tb, const int32_t* ids, const Outputs& out,
                                  uint32_t* status, const void* x, void* dst, bool direct, int vec, hipStream_t st);
 // Whether pack runs in gather form (one wavefront per send place, reading the token the

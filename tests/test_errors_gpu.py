@@ -70,8 +70,8 @@ def test_host_side_rejections_enqueue_nothing():
 
 
 # 64 tokens per rank: one-launch dispatch (512 assignments), with 4 KB rows also with
-# each row's count split over a block's wavefronts; 300: planned (2400)
-@pytest.mark.parametrize("tokens,hidden", [(64, 96), (64, 2048), (300, 96)],
+# each row's count split over a block's wavefronts; 1100: planned (8800)
+@pytest.mark.parametrize("tokens,hidden", [(64, 96), (64, 2048), (1100, 96)],
                          ids=["one-launch", "one-launch-split-count", "planned"])
 @pytest.mark.parametrize("layout", [a2av.LAYOUT_SOURCE_MAJOR, a2av.LAYOUT_EXPERT_MAJOR], ids=["srcmaj", "expmaj"])
 @pytest.mark.parametrize("path", [a2av.PATH_STAGED, a2av.PATH_DIRECT], ids=["staged", "direct"])
@@ -368,8 +368,8 @@ def _dest_ids(counts, T):
 
 @pytest.mark.parametrize("name,over,path,expected", [
     # planned form: plan, pack, exchange / return, combine (staged); plan, pack / combine (direct)
-    ("decode", dict(tokens_per_rank=300), a2av.PATH_STAGED, [1, 1, 1, 1, 1]),
-    ("decode", dict(tokens_per_rank=300), a2av.PATH_DIRECT, [1, 1, 0, 0, 1]),
+    ("decode", dict(tokens_per_rank=600), a2av.PATH_STAGED, [1, 1, 1, 1, 1]),
+    ("decode", dict(tokens_per_rank=600), a2av.PATH_DIRECT, [1, 1, 0, 0, 1]),
     # one-launch form: its single launch counts as pack
     ("decode", {}, a2av.PATH_STAGED, [0, 1, 1, 1, 1]),
     ("decode", {}, a2av.PATH_DIRECT, [0, 1, 0, 0, 1]),

@@ -31,9 +31,9 @@ def _tables(w, steps):
 
 @pytest.mark.parametrize("path,layout", [(a2av.PATH_STAGED, 0), (a2av.PATH_DIRECT, 0), (a2av.PATH_DIRECT, 1)],
                          ids=["staged", "direct", "direct-expmaj"])
-# decode and edge dispatch in one launch; the 512-token decode plans first
+# decode and edge dispatch in one launch; the 640-token decode plans first
 @pytest.mark.parametrize("name,over,steps,full_every", [("decode", {}, 100, 10), ("edge", {}, 24, 1),
-                                                        ("decode", dict(tokens_per_rank=512), 24, 8)],
+                                                        ("decode", dict(tokens_per_rank=640), 24, 8)],
                          ids=["decode", "edge", "decode-planned"])
 def test_graph_replay_with_device_side_routing(name, over, steps, full_every, path, layout):
     w = W.workload(name, **over)

@@ -92,17 +92,23 @@ SMALL = [
     # cut into 4 pieces, each row's count split over the block's four wavefronts
     ("wide", dict(num_ranks=16, tokens_per_rank=8, hidden=64, experts_per_rank=4, top_k=7)),
     ("wide", dict(num_ranks=4, tokens_per_rank=16, hidden=2048, experts_per_rank=4, top_k=7)),
-    # one-launch dispatch at its limits (256 assignments per rank, 2048 in all), and just
-    # past each of them
-    ("decode", dict(num_ranks=8, tokens_per_rank=256, hidden=256)),
-    ("decode", dict(num_ranks=8, tokens_per_rank=257, hidden=256)),
-    ("decode", dict(num_ranks=16, tokens_per_rank=129, hidden=256)),
+    # one-launch dispatch at its limits, and just past each of them: 4096 assignments at
+    # top-1 (planning blocks ranking 512 ids each in batches), 1024 per rank, 2048 with
+    # several slots per row on the zero-copy path (4096 on the staged path)
+    ("decode", dict(num_ranks=8, tokens_per_rank=512, hidden=256)),
+    ("decode", dict(num_ranks=8, tokens_per_rank=513, hidden=256)),
+    ("decode", dict(num_ranks=4, tokens_per_rank=1024, hidden=256)),
+    ("decode", dict(num_ranks=2, tokens_per_rank=1025, hidden=256)),
+    ("wide", dict(num_ranks=8, tokens_per_rank=128, hidden=64, experts_per_rank=4, top_k=2)),
+    ("wide", dict(num_ranks=8, tokens_per_rank=129, hidden=64, experts_per_rank=4, top_k=2)),
+    ("wide", dict(num_ranks=8, tokens_per_rank=256, hidden=64, experts_per_rank=4, top_k=2)),
+    ("wide", dict(num_ranks=8, tokens_per_rank=257, hidden=64, experts_per_rank=4, top_k=2)),
     # a small receive capacity (rows dropped, flagged, counts kept)
     ("wide", dict(num_ranks=4, tokens_per_rank=30, hidden=64, experts_per_rank=2, top_k=2,
                   recv_capacity_rows=20)),
     # the same at top-1: the one-launch dispatch, then the planned gather-form pack
     ("decode", dict(num_ranks=4, tokens_per_rank=30, hidden=64, recv_capacity_rows=20)),
-    ("decode", dict(num_ranks=4, tokens_per_rank=300, hidden=64, recv_capacity_rows=200)),
+    ("decode", dict(num_ranks=4, tokens_per_rank=1100, hidden=64, recv_capacity_rows=800)),
     # more assignments per wavefront than its registers hold: planning in several batches
     ("wide", dict(num_ranks=2, tokens_per_rank=9000, hidden=16, experts_per_rank=8, top_k=2)),
     ("wide", dict(num_ranks=8, tokens_per_rank=2000, hidden=16, experts_per_rank=512, top_k=4)),
@@ -155,9 +161,10 @@ def test_repeated_ids_within_a_token_are_sent_k_times(path):
     _full_oracle_check(w, x, ids, gates, path)
 
 
-# Steps of at most 2048 assignments (and at most 256 per rank) dispatch in one launch that
-# places rows by counting over the ids; larger ones plan first.  Cases that probe error
-# handling run on both sides of that line.
+# Small steps (at most 1024 assignments per rank, and at most 2048 in all, 4096 on the
+# staged path or at top-1) dispatch in one launch that places rows by counting over the
+# ids; larger ones plan first.  Cases that probe error handling run on both sides of that
+# line.
 
 
 @pytest.mark.parametrize("tokens", [128, 600], ids=["one-launch", "planned"])
@@ -175,7 +182,7 @@ def test_every_token_routed_to_the_same_two_experts(path, layout, tokens):
     assert int(ref["recv_off"][2, 4]) == 4 * tokens * 2
 
 
-@pytest.mark.parametrize("tokens,hidden", [(24, 128), (16, 2048), (300, 128), (3000, 64)],
+@pytest.mark.parametrize("tokens,hidden", [(24, 128), (16, 2048), (1100, 128), (3000, 64)],
                          ids=["one-launch", "one-launch-split-count", "planned", "planned-in-chunks"])
 @pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
 def test_out_of_range_ids_are_dropped_and_flagged(path, tokens, hidden):
