@@ -62,8 +62,8 @@ bool small_dispatch(const Shape& sh, bool direct);
 hipError_t launch_dispatch_small(const Shape& sh, const Tables& tb, const int32_t* ids, const Outputs& out,
                                  uint32_t* status, const void* x, void* dst, bool direct, int vec, hipStream_t st);
 // Whether pack runs in gather form (one wavefront per send place, reading the token the
-// planner put there; top-1 only, where it moves no more bytes than the scatter form).
-// Planning writes `inv` exactly when this holds.
+// planner put there; top-1 only, where it moves no more bytes than the scatter form, and
+// only at streaming sizes).  Planning writes `inv` exactly when this holds.
 bool gather_pack(const Shape& sh);
 // pack: staged (dst = send buffer) or direct (dst = receive buffer); also builds the
 // receive tables (and the caller's copies in `out`) and, for expert-major buffers, the
