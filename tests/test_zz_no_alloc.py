@@ -1,8 +1,8 @@
 """The allocation-free bare collective (a2av_alltoallv_noalloc) against the handle-based
 one (a2av_alltoallv), through the C ABI: identical receive rows, counts, offsets and
 status on consecutive calls that share the library's one scratch array, the second
-call smaller than the first; the largest rank count it accepts; shapes past its limit
-rejected on the host."""
+call smaller than the first, and at a streaming size; the largest rank count it
+accepts; shapes past its limit rejected on the host."""
 import numpy as np
 import pytest
 import torch
@@ -15,15 +15,16 @@ from tests.gpu_util import banner, host_bits
 pytestmark = pytest.mark.gpu
 
 
-def _inputs(R, T, H, seed):
-    """Sorted per-sender destinations, their counts, and bf16 token rows."""
+def _inputs(R, T, H, seed, cap=0):
+    """Sorted per-sender destinations, their counts, and bf16 token rows (receive capacity
+    cap rows per rank, 0: the worst case)."""
     rng = np.random.default_rng(seed)
     dest = np.sort(rng.integers(0, R, size=(R, T)), axis=1).astype(np.int32)
     if R > 2:
         dest[1] = 0                                   # one sender, one peer
         dest[2, :] = np.sort(rng.integers(0, 2, size=T))   # zero-length segments to the rest
     counts = np.stack([np.bincount(dest[s], minlength=R) for s in range(R)]).astype(np.int32)
-    w = W.Workload("noalloc", R, T, H, W.BF16, 1, 1, "uniform", "softmax", 0, seed=seed)
+    w = W.Workload("noalloc", R, T, H, W.BF16, 1, 1, "uniform", "softmax", 0, seed=seed, recv_capacity_rows=cap)
     return w, dest, counts, W.make_x(w)
 
 
@@ -39,7 +40,7 @@ def _both(w, counts, x, bad_counts=None):
     """Runs the handle-based and the no-alloc collective on the same inputs; returns the
     host copies of (recv, recv_counts, recv_offsets, status) of each."""
     R, T, H, cap = w.num_ranks, w.tokens_per_rank, w.hidden, w.capacity
-    cfg = a2av.make_config(R, T, H, W.BF16, 1, 1)
+    cfg = a2av.make_config(R, T, H, W.BF16, 1, 1, w.recv_capacity_rows)
     xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
     sc = torch.from_numpy(counts if bad_counts is None else bad_counts).cuda()
     outs = []
@@ -74,6 +75,25 @@ def test_noalloc_matches_handle_collective_on_consecutive_calls(shapes):
         for d in range(R):
             n = int(ref["recv_off"][d, R])
             assert np.array_equal(got[0][d, :n], want[d, :n]), f"call {i}: receive rows of rank {d}"
+
+
+def test_noalloc_matches_handle_collective_at_streaming_size():
+    """335 MB of send rows (4 ranks x 8192 rows of 10 KiB): the collective's non-temporal,
+    two-blocks-per-CU copy form, from the scratch tables as from the handle's."""
+    R, T, H = 4, 8192, 5120
+    banner(f"no-alloc streaming call: R={R} T={T} H={H}")
+    w, dest, counts, x = _inputs(R, T, H, seed=21, cap=3 * T)
+    ref_handle, got = _both(w, counts, x)
+    for a, b, name in zip(ref_handle, got, ("recv", "recv_counts", "recv_offsets", "status")):
+        assert np.array_equal(a, b), f"{name} differs from a2av_alltoallv"
+    assert int(got[3][0]) == 0
+    ref = oracle.dispatch(oracle.as_rows(x), dest[..., None], 1, w.capacity)
+    assert np.array_equal(got[1], ref["recv_counts"])
+    assert np.array_equal(got[2], ref["recv_off"])
+    want = ref["recv"].view(np.uint16).reshape(R, w.capacity, H)
+    for d in range(R):
+        n = int(ref["recv_off"][d, R])
+        assert np.array_equal(got[0][d, :n], want[d, :n]), f"receive rows of rank {d}"
 
 
 def test_noalloc_flags_bad_counts_like_the_handle_collective():
