@@ -540,15 +540,17 @@ def decode_graph(np, torch, a2av, W, path, workload="decode", steps=100, per_gra
     if light:
         ok = int(s.status.item()) == 0
         t_dispatch, t_combine = t_route_dispatch - t_route, t_full - t_route_dispatch_expert
+        # how many launches the library's dispatch made, from its own stage timing (no
+        # planning launch: the one-launch form)
+        route()
+        a2av.a2av_timing_begin(s.handle, 1)
+        s.dispatch(xt, ids)
+        _, launches = a2av.a2av_timing_end(s.handle)
         del ref_src, ref_dst
         s.close()
         torch.cuda.empty_cache()
         return {"tokens_per_rank": w.tokens_per_rank, "assignments": w.assignments,
-                # the library's rule for dispatching in one launch (include/a2av.h)
-                "one_launch_dispatch": bool(w.tokens_per_rank > 0 and w.tokens_per_rank * w.top_k <= 1024
-                                            and w.num_experts <= 1024
-                                            and (w.assignments <= 2048 or (w.assignments <= 4096 and (
-                                                path_id == a2av.PATH_STAGED or w.top_k == 1)))),
+                "one_launch_dispatch": launches[0] == 0,
                 "us_dispatch": round(t_dispatch, 2), "us_combine": round(t_combine, 2),
                 "us_reference_copy": round(t_copy, 2), "bytes_dispatch": (w.tokens + w.assignments) * w.row_bytes,
                 "status_ok": ok}
