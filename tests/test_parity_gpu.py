@@ -294,6 +294,20 @@ def test_streaming_sizes_with_two_byte_vectors():
     _check_at_size(w)
 
 
+@pytest.mark.parametrize("name,over", [
+    # top-1: the gather-form pack and the single-slot combine on rows of four-float vectors
+    ("prefill", dict(tokens_per_rank=4096, hidden=2560, dtype=W.F32)),
+    # top-2: the top-k pack through the caches and the paired-slot combine
+    ("wide", dict(num_ranks=8, tokens_per_rank=2048, hidden=2048, dtype=W.F32, experts_per_rank=16, top_k=2)),
+], ids=["top1", "top2"])
+def test_streaming_sizes_in_float32(name, over):
+    # float32 rows at sizes where every row kernel streams (the workloads that reach those
+    # sizes are bf16)
+    w = W.workload(name, **over)
+    assert w.assignments * w.row_bytes >= 256 << 20
+    _check_at_size(w)
+
+
 def _check_at_size(w: W.Workload):
     name = w.name
     banner(f"full size {w.describe()} cap={w.capacity}")
