@@ -316,6 +316,11 @@ def main():
         result["decode_sweep"] = {"path": sweep_path, "workload": W.workload("decode").describe(), "points": [
             decode_graph(np, torch, a2av, W, sweep_path, steps=50, over={"tokens_per_rank": t}, light=True)
             for t in (16, 32, 64, 128, 256, 384, 512, 768, 1024)]}
+        # the same for the top-8 shape (16 ranks, 14 KiB rows, 256 experts) at decode batch sizes
+        result["decode_sweep_top8"] = {"path": sweep_path, "workload": W.workload("wide").describe(), "points": [
+            decode_graph(np, torch, a2av, W, sweep_path, workload="wide", steps=50, over={"tokens_per_rank": t},
+                         light=True)
+            for t in (4, 8, 16, 32, 64, 128)]}
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w)
