@@ -158,7 +158,8 @@ int64_t a2av_workspace_bytes(const a2av_config_t* cfg);
  * The direct path fuses 3 and 4: each row goes from x straight to its receive place
  * (the pages' zero-copy transfer, user buffer to peer user buffer).  Steps of at most
  * 1024 experts and 1024 assignments per rank run 1-3 as a single launch when they hold
- * at most 2048 assignments, or at most 4096 on the staged path or at top-1: every row
+ * at most 2048 assignments, or at most 4096 on the staged path or with rows of at least
+ * 8 KiB: every row
  * finds its place by counting, over topk_ids, the assignments before it in its
  * destination's order (the same place the scans give).  The results are identical.
  * x (device) [R][T][H] dtype; topk_ids (device) [R][T][k].  recv (device, caller

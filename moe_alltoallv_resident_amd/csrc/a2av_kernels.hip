@@ -1429,18 +1429,19 @@ bool small_dispatch(const Shape& sh, bool direct) {
     // The one launch pays off while counting a row's place over the ids costs less than
     // the planning launch it saves.  A row of the staged path counts over its own
     // sender's ids only; a zero-copy row over every id of the senders before it, once per
-    // slot.  Same-box graph A/B against plan + pack, decode shape (8 ranks, 10 KiB rows):
-    // 320 / 512 tokens per rank top-1 zero-copy 15.2 -> 10.4 / 20.3 -> 17.9 us, staged
-    // 26.7 -> 22.8 / 37.5 -> 35.1 us; 16 ranks x 256 and 32 x 128 tokens 20.1 -> 17.5 and
-    // 19.9 -> 17.6 us; past 4096 assignments the zero-copy count lost (768 tokens 27.0 ->
-    // 29.5 us), and with several slots per row at 2,048-4,096 assignments it lost too
-    // (64 ranks x 32 tokens top-2 9.9 -> 13.4 us, 8 ranks x 64 tokens top-8 18.4 -> 30.2),
-    // while the staged form still gained there (21.9 -> 18.2, 44.9 -> 44.5 us).  Each
+    // slot, which long rows (more bytes to move behind the count) hide better.  Same-box
+    // graph A/B against plan + pack: decode shape (8 ranks, 10 KiB rows) 320 / 512 tokens
+    // per rank top-1 zero-copy 15.2 -> 10.4 / 20.3 -> 17.9 us, staged 26.7 -> 22.8 /
+    // 37.5 -> 35.1 us; 16 ranks x 256 and 32 x 128 tokens 20.1 -> 17.5 and 19.9 -> 17.6
+    // us; top-2 at 200 tokens 13.9 -> 10.8 us; top-8 (14 KiB rows) 16 ranks x 24 / 32
+    // tokens 16.4 -> 12.3 / 18.7 -> 15.8 us; past 4096 assignments the zero-copy count lost
+    // (768 tokens 27.0 -> 29.5 us), and so it did with 4 KiB rows (64 ranks x 32 tokens
+    // top-2 9.95 -> 11.6 us) while the staged form gained there (21.9 -> 18.2 us).  Each
     // planning block ranks its rank's ids in 64-assignment batches per wavefront (up to
     // 1,024 per rank); the ids stay in LDS beside the counters (at most 16 KiB).
     const int64_t A = (int64_t)sh.R * sh.TK;
     if (sh.T == 0 || sh.TK > 1024 || sh.E > 1024) return false;
-    return A <= 2048 || (A <= 4096 && (!direct || sh.k == 1));
+    return A <= 2048 || (A <= 4096 && (!direct || sh.row_bytes >= 8192));
 }
 
 hipError_t launch_dispatch_small(const Shape& sh, const Tables& tb, const int32_t* ids, const Outputs& out,

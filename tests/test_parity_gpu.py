@@ -92,13 +92,16 @@ SMALL = [
     # cut into 4 pieces, each row's count split over the block's four wavefronts
     ("wide", dict(num_ranks=16, tokens_per_rank=8, hidden=64, experts_per_rank=4, top_k=7)),
     ("wide", dict(num_ranks=4, tokens_per_rank=16, hidden=2048, experts_per_rank=4, top_k=7)),
-    # one-launch dispatch at its limits, and just past each of them: 4096 assignments at
-    # top-1 (planning blocks ranking 512 ids each in batches), 1024 per rank, 2048 with
-    # several slots per row on the zero-copy path (4096 on the staged path)
+    # one-launch dispatch at its limits, and just past each of them: 4096 assignments
+    # with rows of 8 KiB or more (planning blocks ranking 512 ids each in batches), 1024
+    # per rank, 2048 with shorter rows on the zero-copy path (4096 on the staged path)
+    ("decode", dict(num_ranks=8, tokens_per_rank=512, hidden=4096)),
+    ("decode", dict(num_ranks=8, tokens_per_rank=513, hidden=4096)),
+    ("decode", dict(num_ranks=4, tokens_per_rank=1024, hidden=4096)),
+    ("decode", dict(num_ranks=2, tokens_per_rank=1025, hidden=4096)),
+    ("wide", dict(num_ranks=8, tokens_per_rank=256, hidden=4096, experts_per_rank=4, top_k=2)),
+    ("wide", dict(num_ranks=8, tokens_per_rank=257, hidden=4096, experts_per_rank=4, top_k=2)),
     ("decode", dict(num_ranks=8, tokens_per_rank=512, hidden=256)),
-    ("decode", dict(num_ranks=8, tokens_per_rank=513, hidden=256)),
-    ("decode", dict(num_ranks=4, tokens_per_rank=1024, hidden=256)),
-    ("decode", dict(num_ranks=2, tokens_per_rank=1025, hidden=256)),
     ("wide", dict(num_ranks=8, tokens_per_rank=128, hidden=64, experts_per_rank=4, top_k=2)),
     ("wide", dict(num_ranks=8, tokens_per_rank=129, hidden=64, experts_per_rank=4, top_k=2)),
     ("wide", dict(num_ranks=8, tokens_per_rank=256, hidden=64, experts_per_rank=4, top_k=2)),
