@@ -159,9 +159,9 @@ int64_t a2av_workspace_bytes(const a2av_config_t* cfg);
  * (the pages' zero-copy transfer, user buffer to peer user buffer).  Steps of at most
  * 1024 experts and 1024 assignments per rank run 1-3 as a single launch when they hold
  * at most 2048 assignments, or at most 4096 on the staged path or with rows of at least
- * 8 KiB: every row
- * finds its place by counting, over topk_ids, the assignments before it in its
- * destination's order (the same place the scans give).  The results are identical.
+ * 8 KiB: every row finds its place by counting, over topk_ids, the assignments before
+ * it in its destination's order (the same place the scans give).  The results are
+ * identical.
  * x (device) [R][T][H] dtype; topk_ids (device) [R][T][k].  recv (device, caller
  * owned) [R][cap][H]: only the first min(recv_offsets[d][R], cap) rows of slice d are
  * written.  split, recv_counts, recv_offsets (device, optional: NULL = not wanted)
@@ -277,8 +277,9 @@ int a2av_stream_reference(const void* src, void* dst, int64_t bytes, int32_t mod
 /* Stage timing with HIP events recorded between the library's kernels on the call's
  * stream.  a2av_timing_begin(h, max_calls), 1 <= max_calls <= A2AV_TIMING_MAX_CALLS,
  * creates events for up to max_calls dispatch and max_calls combine calls (host-side
- * event objects only; no device memory); later calls record until the budget is used.  a2av_timing_end waits for
- * the recorded events, writes per-stage sums of milliseconds into ms_sum (host)
+ * event objects only; no device memory); later calls record until the budget is used.
+ * a2av_timing_end waits for the recorded events, writes per-stage sums of
+ * milliseconds into ms_sum (host)
  * [A2AV_STAGES] and the number of timed launches per stage into launches (host)
  * [A2AV_STAGES], and releases the events.  Stages: 0 plan (histogram + scans), 1 pack,
  * 2 exchange, 3 return exchange, 4 combine (the direct path has no 2 and 3; a
