@@ -90,6 +90,11 @@ typedef struct a2av_context* a2av_handle_t;
 /* device status bits, OR-ed into *status */
 #define A2AV_ST_EXPERT_RANGE  1u  /* an expert id was outside [0, E): that slot is dropped */
 #define A2AV_ST_RECV_OVERFLOW 2u  /* a rank received more rows than recv_capacity_rows */
+#define A2AV_ST_BOUNDS        4u  /* debug build only (liba2av_debug.so, compiled with
+                                     A2AV_DEBUG=1): a device-side bounds check on a row
+                                     index or a table value failed and that access was
+                                     skipped.  The release library has the same exports
+                                     and results and never sets it. */
 
 /* data paths (a2av_config_t.path) */
 #define A2AV_PATH_STAGED 0        /* pack into send segments, exchange, return, combine */

@@ -21,6 +21,7 @@ NOALLOC_MAX_RANKS = 256
 NOALLOC_SCRATCH_BYTES = 1 << 20
 ST_EXPERT_RANGE = 1
 ST_RECV_OVERFLOW = 2
+ST_BOUNDS = 4
 EXPERT_IDENTITY = 0
 EXPERT_SCALE = 1
 PATH_STAGED = 0
@@ -33,7 +34,10 @@ STREAM_WRITE = 1
 STREAM_READ_OUT_BYTES = 1 << 20
 STAGE_NAMES = ("plan", "pack", "exchange", "return", "combine")
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liba2av.so")
+# A2AV_DEBUG=1 in the environment selects the debug build (device-side bounds checks,
+# status bit ST_BOUNDS); same exports and results.
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                        "liba2av_debug.so" if os.environ.get("A2AV_DEBUG") == "1" else "liba2av.so")
 EXPORTS = ("a2av_create", "a2av_destroy", "a2av_workspace_bytes", "a2av_dispatch", "a2av_combine",
            "a2av_alltoallv", "a2av_alltoallv_noalloc", "a2av_copy_positions", "a2av_copy_recv_expert_offsets",
            "a2av_copy_send_offsets", "a2av_expert_apply", "a2av_route_step", "a2av_copy_reference",

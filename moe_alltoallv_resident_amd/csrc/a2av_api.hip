@@ -177,6 +177,7 @@ DeviceScratch g_scratch[kMaxDevices];
 static __device__ __align__(256) unsigned char scratch[A2AV_NOALLOC_SCRATCH_BYTES];
 
 static_assert(A2AV_NOALLOC_MAX_RANKS <= a2av::kMaxRanks, "no-alloc rank limit");
+static_assert(A2AV_ST_BOUNDS == a2av::kStBounds, "debug status bit");
 
 namespace {
 
@@ -339,7 +340,7 @@ int a2av_combine(a2av_handle_t h, const void* expert_out, const float* gates, vo
     }
     const void* rows = h->direct ? expert_out : h->send_buf;
     return launch_timed(h, kStageCombine, st,
-                        [&] { return a2av::launch_combine(sh, tb, rows, gates, y, h->direct, vec, st); });
+                        [&] { return a2av::launch_combine(sh, tb, rows, gates, y, status, h->direct, vec, st); });
 }
 
 int a2av_alltoallv(a2av_handle_t h, const void* send, const int32_t* send_counts, void* recv, int32_t* recv_counts,

@@ -76,7 +76,7 @@ hipError_t launch_exchange(const Shape& sh, const Tables& tb, const Outputs& out
                            const void* src, void* dst, bool reverse, bool first, int vec, hipStream_t st);
 // combine: rows = return buffer (staged) or expert outputs in the receive layout (direct).
 hipError_t launch_combine(const Shape& sh, const Tables& tb, const void* rows, const float* gates, void* y,
-                          bool direct, int vec, hipStream_t st);
+                          uint32_t* status, bool direct, int vec, hipStream_t st);
 hipError_t launch_expert(const Shape& sh, const Tables& tb, const void* in, void* out, int mode, int vec,
                          hipStream_t st);
 hipError_t launch_reference_copy(const void* src, void* dst, int64_t rows, int64_t row_bytes, int num_cu,
@@ -91,5 +91,8 @@ constexpr int32_t kMaxExperts = 4096;
 static_assert(3 * 4 * kMaxExperts <= kPlanLdsBytes, "planning LDS budget");
 constexpr int32_t kMaxRanks = 1024;
 constexpr int32_t kMaxTopK = 64;
+
+// Status bit of the debug build's device-side bounds checks (A2AV_ST_BOUNDS).
+constexpr uint32_t kStBounds = 4u;
 
 }  // namespace a2av

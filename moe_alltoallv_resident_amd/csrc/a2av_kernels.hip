@@ -60,6 +60,35 @@ __device__ __forceinline__ uint64_t lanes_below(int lane) {
     return lane == 0 ? 0ull : (~0ull >> (kWave - lane));
 }
 
+// ---- debug build ---------------------------------------------------------------------
+// Built with -DA2AV_DEBUG=1 (liba2av_debug.so), the kernels of the path check every row
+// index they form against the rows of the buffer it addresses before the access, and
+// every table value they turn into an index against its range; a failed check ORs
+// kStBounds into the call's status word and the access is skipped.  The release build
+// compiles the checks away: there the same indices are in range by construction
+// (receive places checked against the capacity, send places against the rows a sender
+// sends, ids against [0, E)).
+#ifndef A2AV_DEBUG
+#define A2AV_DEBUG 0
+#endif
+// Whether 0 <= i < n (always true in the release build).
+__device__ __forceinline__ bool row_ok(uint32_t* status, int64_t i, int64_t n) {
+    if constexpr (A2AV_DEBUG != 0) {
+        if ((uint64_t)i < (uint64_t)n) return true;
+        atomicOr(status, kStBounds);
+        return false;
+    } else {
+        return true;
+    }
+}
+// Flags a value that the release code already steps around but that no correct table
+// holds (debug build only).
+__device__ __forceinline__ void flag_if(uint32_t* status, bool bad) {
+    if constexpr (A2AV_DEBUG != 0) {
+        if (bad) atomicOr(status, kStBounds);
+    }
+}
+
 // Inclusive prefix sum across the 64 lanes of a wavefront.
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
     const int lane = lane_id();
@@ -304,8 +333,11 @@ __device__ void plan_rank(const PlanArgs& a, int s, int c, int C, int* lds, int*
     auto put = [&](int64_t i, int p) {
         pos[i] = p;
         if (a.inverse) {
-            if (p >= 0) inv[p] = (int32_t)i;
-            else dest[i] = -1;
+            if (p >= 0) {
+                if (row_ok(a.status, p, TK)) inv[p] = (int32_t)i;
+            } else {
+                dest[i] = -1;
+            }
         }
     };
     if (one_batch) {
@@ -539,6 +571,7 @@ __global__ void __launch_bounds__(RPB * kWave) pack_kernel(const V* __restrict__
         for (int j = 0; j < k; ++j) {
             const int pj = __builtin_amdgcn_readlane(my, j);
             if (pj < 0 || pj >= sh.TK) {              // dropped slot (never out of the buffer)
+                flag_if(status, pj >= sh.TK);
                 if (DIRECT && record) tb.dest[n * k + j] = -1;
                 continue;
             }
@@ -548,9 +581,10 @@ __global__ void __launch_bounds__(RPB * kWave) pack_kernel(const V* __restrict__
                 const int64_t q = d >= R ? -1          // not a sent row (tables always place it)
                                          : sh.layout ? expert_major_place_counted(sh, tb, s, pj, d, lane)
                                                      : recv_base(tb.send_off, R, d, (int)s, lane) + (pj - so[d]);
+                flag_if(status, q < 0);
                 const int64_t rr = q >= 0 && q < sh.cap ? (int64_t)d * sh.cap + q : -1;   // past capacity: flagged
                 if (record) tb.dest[n * k + j] = rr;
-                if (rr < 0) continue;
+                if (rr < 0 || !row_ok(status, rr, (int64_t)R * sh.cap)) continue;
                 row = dst + rr * nvec;
             } else {
                 row = dst + (s * sh.TK + pj) * nvec;
@@ -592,15 +626,18 @@ __global__ void __launch_bounds__(RPB * kWave) pack_gather_kernel(const V* __res
     const int64_t s = g / sh.TK, p = g - s * sh.TK;
     const int32_t* so = tb.send_off + s * (R + 1);
     if (p >= so[R]) return;                          // not a sent row
-    const int64_t n = s * sh.T + tb.inv[g];          // its token (k = 1: the assignment is the token)
+    const int32_t t = tb.inv[g];
+    if (!row_ok(status, t, sh.T)) return;
+    const int64_t n = s * sh.T + t;                  // its token (k = 1: the assignment is the token)
     int64_t row = g;
     if constexpr (DIRECT) {
         const int d = segment_of(so, R, p, lane);    // < R, since p < so[R]
         const int64_t q = sh.layout ? expert_major_place_counted(sh, tb, s, p, d, lane)
                                     : recv_base(tb.send_off, R, d, (int)s, lane) + (p - so[d]);
-        row = q < sh.cap ? (int64_t)d * sh.cap + q : -1;   // past capacity: flagged by the tables
+        flag_if(status, q < 0);
+        row = q >= 0 && q < sh.cap ? (int64_t)d * sh.cap + q : -1;   // past capacity: flagged by the tables
         if (pc.v0 == 0 && lane == 0) tb.dest[n] = row;
-        if (row < 0) return;
+        if (row < 0 || !row_ok(status, row, (int64_t)R * sh.cap)) return;
     }
     copy_row<V, U, NT>(dst + row * nvec, x + n * nvec, pc.v0, pc.v1, lane);
 }
@@ -840,10 +877,11 @@ __global__ void __launch_bounds__(kBlock) dispatch_small_kernel(const V* __restr
     }
     // the first piece of a row records where its slots went (for the combine)
     if (DIRECT && pc.v0 == 0 && lane < k) a.tb.dest[n * k + lane] = my_row;
+    const int64_t dst_rows = DIRECT ? (int64_t)R * sh.cap : A;
     for (;;) {
         for (int j = 0; j < k; ++j) {
             const int64_t rj = __shfl(my_row, j, kWave);
-            if (rj < 0) continue;
+            if (rj < 0 || !row_ok(a.status, rj, dst_rows)) continue;
             V* row = dst + rj * nvec;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -901,7 +939,10 @@ __global__ void __launch_bounds__(RPB * kWave) exchange_kernel(const V* __restri
     else if (sh.layout) q = expert_major_place(sh, tb, s, p, d, lane);
     else q = (int64_t)tb.recv_off[(int64_t)d * (R + 1) + s] + (p - so[d]);
     const int64_t send_row = s * sh.TK + p, recv_row = (int64_t)d * sh.cap + q;
+    flag_if(status, q < 0);
     const bool in_cap = q >= 0 && q < sh.cap;
+    if (!row_ok(status, send_row, (int64_t)R * sh.TK) || (in_cap && !row_ok(status, recv_row, (int64_t)R * sh.cap)))
+        return;
     if (!REVERSE) {
         if (!in_cap) return;
         if constexpr (kLoadsFirst) {
@@ -931,7 +972,7 @@ __global__ void __launch_bounds__(RPB * kWave) exchange_kernel(const V* __restri
 template <typename V, int U, bool NT, int RPB>
 __global__ void __launch_bounds__(RPB * kWave) exchange_recv_order_kernel(const V* __restrict__ src,
                                                                           V* __restrict__ dst, Shape sh, Tables tb,
-                                                                          Split sp) {
+                                                                          uint32_t* status, Split sp) {
     const int lane = lane_id();
     const Piece pc = piece_of((int64_t)blockIdx.x * RPB + threadIdx.x / kWave, sp);
     const int64_t g = pc.row;
@@ -958,6 +999,7 @@ __global__ void __launch_bounds__(RPB * kWave) exchange_recv_order_kernel(const 
     const int32_t* ro = tb.recv_off + (int64_t)d * (R + 1);
     const int s = segment_of(ro, R, q, lane);        // < R: q < ro[R]
     const int64_t p = (int64_t)tb.send_off[(int64_t)s * (R + 1) + d] + (q - ro[s]);
+    if (!row_ok(status, s, R) || !row_ok(status, p, sh.TK) || !row_ok(status, q, sh.cap)) return;
     copy_row<V, U, NT>(dst + ((int64_t)d * sh.cap + q) * sp.nvec, src + ((int64_t)s * sh.TK + p) * sp.nvec, pc.v0,
                        pc.v1, lane);
 }
@@ -1024,7 +1066,7 @@ template <int B, int DT, int U, bool NT, bool DIRECT, bool PAIRS, int RPB>
 __global__ void __launch_bounds__(RPB * kWave) combine_kernel(const typename Vec<B>::T* __restrict__ rows,
                                                          const float* __restrict__ gates,
                                                          typename Vec<B>::T* __restrict__ y, Shape sh, Tables tb,
-                                                         Split sp) {
+                                                         uint32_t* status, Split sp) {
     using V = typename Vec<B>::T;
     using El = Elems<B, DT>;
     constexpr int NE = El::N;
@@ -1043,9 +1085,11 @@ __global__ void __launch_bounds__(RPB * kWave) combine_kernel(const typename Vec
     if constexpr (DIRECT) {
         if (lane < k) {
             const int64_t r = tb.dest[n * k + lane];
+            flag_if(status, r < -1 || r >= (int64_t)R * sh.cap);
             if (r >= 0 && r < (int64_t)R * sh.cap) my_row = r;
         }
     } else {
+        flag_if(status, lane < k && (my_p < -1 || my_p >= sh.TK));
         if (my_p >= 0 && my_p < sh.TK) my_row = s * sh.TK + my_p;
     }
     V* out = y + n * nvec;
@@ -1504,7 +1548,7 @@ hipError_t launch_exchange(const Shape& sh, const Tables& tb, const Outputs& out
                 else if (!sh.layout && nt)   // streaming sizes only: at decode sizes the extra
                                              // dependent search made the staged step 8 % slower
                     hipLaunchKernelGGL((exchange_recv_order_kernel<V, u, nt, kRowsPerBlock>), dim3(grid), dim3(kBlock),
-                                       lds, st, (const V*)src, (V*)dst, sh, tb, sp);
+                                       lds, st, (const V*)src, (V*)dst, sh, tb, status, sp);
                 else
                     hipLaunchKernelGGL((exchange_kernel<V, u, nt, false, false, kRowsPerBlock>), dim3(grid),
                                        dim3(kBlock), lds, st, (const V*)src, (V*)dst, sh, tb, out, status, sp);
@@ -1516,7 +1560,7 @@ hipError_t launch_exchange(const Shape& sh, const Tables& tb, const Outputs& out
 
 template <int B, int DT>
 static hipError_t launch_combine_t(const Shape& sh, const Tables& tb, const void* rows, const float* gates, void* y,
-                                   bool direct, hipStream_t st) {
+                                   uint32_t* status, bool direct, hipStream_t st) {
     using V = typename Vec<B>::T;
     const int64_t N = (int64_t)sh.R * sh.T;
     const int64_t bytes = N * sh.row_bytes;
@@ -1538,38 +1582,38 @@ static hipError_t launch_combine_t(const Shape& sh, const Tables& tb, const void
             if (sh.k == 1) {
                 if (direct)
                     hipLaunchKernelGGL((combine_kernel<B, DT, U1, nt, true, false, rpb>), dim3(grid), block, 0, st,
-                                       (const V*)rows, gates, (V*)y, sh, tb, sp);
+                                       (const V*)rows, gates, (V*)y, sh, tb, status, sp);
                 else
                     hipLaunchKernelGGL((combine_kernel<B, DT, U1, nt, false, false, rpb>), dim3(grid), block, 0, st,
-                                       (const V*)rows, gates, (V*)y, sh, tb, sp);
+                                       (const V*)rows, gates, (V*)y, sh, tb, status, sp);
             } else {
                 if (direct)
                     hipLaunchKernelGGL((combine_kernel<B, DT, UK, nt, true, true, rpb>), dim3(grid), block, 0, st,
-                                       (const V*)rows, gates, (V*)y, sh, tb, sp);
+                                       (const V*)rows, gates, (V*)y, sh, tb, status, sp);
                 else
                     hipLaunchKernelGGL((combine_kernel<B, DT, UK, nt, false, true, rpb>), dim3(grid), block, 0, st,
-                                       (const V*)rows, gates, (V*)y, sh, tb, sp);
+                                       (const V*)rows, gates, (V*)y, sh, tb, status, sp);
             }
             return hipGetLastError();
         });
     });
 }
 
-hipError_t launch_combine(const Shape& sh, const Tables& tb, const void* rows, const float* gates, void* y, bool direct,
-                          int vec, hipStream_t st) {
+hipError_t launch_combine(const Shape& sh, const Tables& tb, const void* rows, const float* gates, void* y,
+                          uint32_t* status, bool direct, int vec, hipStream_t st) {
     if ((int64_t)sh.R * sh.T == 0) return hipSuccess;
     if (sh.dtype == 1) {
         switch (vec) {
-            case 16: return launch_combine_t<16, 1>(sh, tb, rows, gates, y, direct, st);
-            case 8: return launch_combine_t<8, 1>(sh, tb, rows, gates, y, direct, st);
-            case 4: return launch_combine_t<4, 1>(sh, tb, rows, gates, y, direct, st);
-            default: return launch_combine_t<2, 1>(sh, tb, rows, gates, y, direct, st);
+            case 16: return launch_combine_t<16, 1>(sh, tb, rows, gates, y, status, direct, st);
+            case 8: return launch_combine_t<8, 1>(sh, tb, rows, gates, y, status, direct, st);
+            case 4: return launch_combine_t<4, 1>(sh, tb, rows, gates, y, status, direct, st);
+            default: return launch_combine_t<2, 1>(sh, tb, rows, gates, y, status, direct, st);
         }
     }
     switch (vec) {
-        case 16: return launch_combine_t<16, 0>(sh, tb, rows, gates, y, direct, st);
-        case 8: return launch_combine_t<8, 0>(sh, tb, rows, gates, y, direct, st);
-        default: return launch_combine_t<4, 0>(sh, tb, rows, gates, y, direct, st);
+        case 16: return launch_combine_t<16, 0>(sh, tb, rows, gates, y, status, direct, st);
+        case 8: return launch_combine_t<8, 0>(sh, tb, rows, gates, y, status, direct, st);
+        default: return launch_combine_t<4, 0>(sh, tb, rows, gates, y, status, direct, st);
     }
 }
 

@@ -32,6 +32,18 @@ def test_library_exports_every_declared_symbol():
         assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
 
 
+def test_debug_library_exports_the_same_symbols():
+    """liba2av_debug.so (A2AV_DEBUG=1: device-side bounds checks) is built beside the
+    release library and exports every declared entry point too."""
+    from moe_alltoallv_resident_amd import build as lib_build
+    dbg = ctypes.CDLL(lib_build.DEBUG_LIB)
+    for name in declared_functions():
+        assert ctypes.cast(getattr(dbg, name), ctypes.c_void_p).value, name
+    assert a2av.ST_BOUNDS == 4
+    header = open(HEADER).read()
+    assert re.search(r"#define A2AV_ST_BOUNDS\s+4u", header)
+
+
 def test_error_strings():
     assert a2av.error_string(a2av.OK) == "ok"
     assert "invalid" in a2av.error_string(a2av.ERR_INVALID)
