@@ -44,6 +44,20 @@ def test_debug_library_exports_the_same_symbols():
     assert re.search(r"#define A2AV_ST_BOUNDS\s+4u", header)
 
 
+def test_environment_selects_the_debug_library():
+    """A2AV_DEBUG=1 makes the binding load liba2av_debug.so (checked in a child process,
+    where the variable is set before the binding is imported)."""
+    import subprocess
+    import sys
+    code = ("from moe_alltoallv_resident_amd import a2av; import os; "
+            "print(os.path.basename(a2av.LIB_PATH), os.path.basename(a2av.lib()._name))")
+    for value, want in (("1", "liba2av_debug.so"), ("0", "liba2av.so")):
+        env = dict(os.environ, A2AV_DEBUG=value)
+        out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True,
+                             timeout=120, check=True).stdout.split()
+        assert out == [want, want], (value, out)
+
+
 def test_error_strings():
     assert a2av.error_string(a2av.OK) == "ok"
     assert "invalid" in a2av.error_string(a2av.ERR_INVALID)
