@@ -932,12 +932,28 @@ __global__ void __launch_bounds__(RPB * kWave) exchange_kernel(const V* __restri
     V r0[U];
     if constexpr (kLoadsFirst) load_chunk<U, NT>(r0, src + (s * sh.TK + p) * nvec, pc.v0, pc.v1, lane);
     const int32_t* so = tb.send_off + s * (R + 1);
-    if (p >= so[R]) return;
-    const int d = segment_of(so, R, p, lane);
+    int d;
     int64_t q;
-    if (FIRST) q = recv_base(tb.send_off, R, d, (int)s, lane) + (p - so[d]);   // the bare collective
-    else if (sh.layout) q = expert_major_place(sh, tb, s, p, d, lane);
-    else q = (int64_t)tb.recv_off[(int64_t)d * (R + 1) + s] + (p - so[d]);
+    if (!NT && !FIRST && !sh.layout && R <= kWave) {
+        // below streaming sizes, source-major, at most 64 ranks: the sender's send offsets
+        // (lane l: so[l]) and every receiver's receive offset for this sender (lane l:
+        // recv_off[l][s]) in one round of loads, then the segment and the place from
+        // registers, where the general form reads them in three dependent rounds
+        const int32_t so_l = so[min(lane, R - 1)];
+        const int32_t so_end = so[R];
+        const int32_t ro_l = tb.recv_off[(int64_t)min(lane, R - 1) * (R + 1) + s];
+        if (p >= so_end) return;
+        const int32_t up = __shfl(so_l, min(lane + 1, kWave - 1), kWave);
+        const int32_t seg_end = lane + 1 < R ? up : so_end;          // so[l + 1]
+        d = __popcll(__ballot(lane < R && seg_end <= p));            // < R, since p < so[R]
+        q = (int64_t)__shfl(ro_l, d, kWave) + (p - __shfl(so_l, d, kWave));
+    } else {
+        if (p >= so[R]) return;
+        d = segment_of(so, R, p, lane);
+        if (FIRST) q = recv_base(tb.send_off, R, d, (int)s, lane) + (p - so[d]);   // the bare collective
+        else if (sh.layout) q = expert_major_place(sh, tb, s, p, d, lane);
+        else q = (int64_t)tb.recv_off[(int64_t)d * (R + 1) + s] + (p - so[d]);
+    }
     const int64_t send_row = s * sh.TK + p, recv_row = (int64_t)d * sh.cap + q;
     flag_if(status, q < 0);
     const bool in_cap = q >= 0 && q < sh.cap;
